@@ -1,0 +1,256 @@
+"""Complete-call benchmark of query-union sparse-attention prefill on one MI355X.
+
+One step = one complete call on resident inputs: the grouping search
+(pw_group) followed by the union attention (pw_union_attention), both on the
+same stream.  Default workload: 64K-token prefill of a Llama-3-8B-like layer
+(32 Q / 8 KV heads, d = 128, page 64, 64 selected pages per (query, KV head),
+Zipf(1.1) community draws, W = 256, g = 8), FP8 e4m3fn KV, bf16 Q and O.
+
+Prints one JSON line (rank 0).  `value` is useful TFLOP/s: 4*D flops per
+(visible selected key, Q head), i.e. only each query's own support.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+METRIC = "complete-call latency (search+attn) & useful TFLOP/s, 64K prefill FP8 KV"
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_64k")
+    ap.add_argument("--no-arms", action="store_true", help="skip the identity / g=1 comparison arms")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle sample time")
+    ap.add_argument("--cold", type=int, default=5, help="cold-cache runs (MALL/L2 flushed)")
+    return ap.parse_args()
+
+
+def union_stats(sel: np.ndarray, ids: np.ndarray, g: int, N: int):
+    """Per-group union sizes (pages) from the selections and the query IDs (host, numpy)."""
+    H, T, S = sel.shape
+    ng = (T + g - 1) // g
+    pad = ng * g - T
+    idp = np.concatenate([ids, np.full((H, pad), -1, ids.dtype)], axis=1) if pad else ids
+    rows = np.where(idp[..., None] >= 0, np.take_along_axis(sel, np.clip(idp, 0, T - 1)[..., None], axis=1), -1)
+    rows = rows.reshape(H, ng, g * S)
+    rows = np.where((rows >= 0) & (rows < N), rows, -1)
+    s = np.sort(rows, axis=2)
+    distinct = s >= 0
+    distinct[:, :, 1:] &= s[:, :, 1:] != s[:, :, :-1]
+    return distinct.sum(axis=2)          # [H][ng]
+
+
+def kernel_hash() -> str:
+    src = os.path.join(ROOT, "query_union_paged_amd", "csrc", "union_attn.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+
+
+def recorded_traffic(per_launch_key: str):
+    """HBM bytes per launch measured with rocprofv3 counters, if taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", "union_attn_counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("kernel_sha256_16") != kernel_hash():
+        return None
+    return rec.get(per_launch_key)
+
+
+def cpu_baseline(inp, wl, seconds: float):
+    """The fp64 oracle on a bounded sample of the same workload (host cores)."""
+    from oracle.attention import Problem, attention_pairs_parallel
+    from oracle.greedy import group_ids
+    from query_union_paged_amd import synth
+    workers = len(os.sched_getaffinity(0))
+    pb = Problem(inp["q_bits"], inp["k_codes"], inp["v_codes"], inp["scales"], inp["sel_pages"])
+    # calibrate on a small stratified sample, then size the timed sample
+    rng = np.random.default_rng(0)
+    def sample(n):
+        t = np.sort(rng.choice(wl.T, size=n, replace=False))
+        return [(h, int(x)) for h in range(wl.H_kv) for x in t]
+    pairs = sample(16)
+    t0 = time.time()
+    attention_pairs_parallel(pb, pairs, workers=workers)
+    per_pair = (time.time() - t0) / len(pairs)
+    n = int(max(16, min(wl.T, seconds / max(per_pair, 1e-6) / wl.H_kv)))
+    pairs = sample(n)
+    t0 = time.time()
+    attention_pairs_parallel(pb, pairs, workers=workers)
+    dt = time.time() - t0
+    sel = inp["sel_pages"]
+    flops = 0.0
+    for h, t in pairs:
+        row = sel[h, t]
+        u = np.unique(row[(row >= 0) & (row < wl.N)]).astype(np.int64)
+        flops += float(np.clip(t - u * wl.P + 1, 0, wl.P).sum()) * wl.G * 4 * wl.D
+    # the CPU greedy search on a sample of windows
+    nwin = max(1, min(32, wl.T // wl.W))
+    t1 = time.time()
+    group_ids(sel, wl.N, wl.W, wl.g, workers=workers,
+              windows={h: list(range(0, nwin * wl.W, wl.W)) for h in range(wl.H_kv)})
+    gdt = time.time() - t1
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": workers, "kind": "oracle",
+        "sample": f"{len(pairs)} (KV head, query) rows ({n} stratified queries x {wl.H_kv} heads), "
+                  f"fp64 numpy, {dt:.1f} s; full-job estimate {dt * wl.T / n:.0f} s",
+        "greedy_windows_per_s": nwin * wl.H_kv / gdt,
+        "greedy_full_estimate_s": gdt * (wl.T // wl.W) / nwin,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the path shards by KV head with no communication; see the design notes).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from query_union_paged_amd import pageweaver as pw
+    from query_union_paged_amd import synth
+
+    wl = synth.WORKLOADS[args.workload]
+    t0 = time.time()
+    inp = synth.make_qkv(wl)
+    inp["sel_pages"] = synth.make_selection(wl, workers=min(16, len(os.sched_getaffinity(0))))
+    log(f"[bench] inputs {wl.name} generated in {time.time() - t0:.1f}s")
+    dev = pw.to_device(inp)
+    shp = pw.shape(*wl.shape_tuple())
+    stream = torch.cuda.current_stream()
+    F_u = synth.useful_flops(inp["sel_pages"], wl)
+
+    ids = pw.pw_group(shp, dev["sel_pages"], wl.W, wl.g)
+    O = pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
+                              dev["sel_pages"], ids, wl.g)
+    torch.cuda.synchronize()
+
+    def step():
+        pw.pw_group(shp, dev["sel_pages"], wl.W, wl.g, query_ids=ids)
+        pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
+                              dev["sel_pages"], ids, wl.g, O=O)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e0, e1, e2 in ev:
+        e0.record(stream)
+        pw.pw_group(shp, dev["sel_pages"], wl.W, wl.g, query_ids=ids)
+        e1.record(stream)
+        pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
+                              dev["sel_pages"], ids, wl.g, O=O)
+        e2.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    search_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
+    attn_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
+    ms_per_step = wall * 1e3 / args.steps
+    value = F_u / (ms_per_step * 1e-3) / 1e12
+
+    # cold runs: a 1 GiB write between runs evicts MALL and L2
+    cold = []
+    if args.cold > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        for _ in range(args.cold):
+            flush.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            cold.append(a.elapsed_time(b))
+        del flush
+
+    # union accounting for the roofline (host-side, from the IDs the search returned)
+    ids_np = ids.cpu().numpy()
+    usz = union_stats(inp["sel_pages"], ids_np, wl.g, wl.N)
+    n_units = int(usz.sum())                       # (group, union page) pairs per launch
+    page_bytes = 2 * wl.P * wl.D                   # K + V e4m3fn bytes of one (page, KV head)
+    qo_bytes = 2 * wl.T * wl.H_q * wl.D * 2
+    meta_bytes = inp["sel_pages"].nbytes * 2 + ids_np.nbytes + inp["scales"].nbytes
+    alg_bytes = n_units * page_bytes + qo_bytes + meta_bytes
+    rows = wl.g * wl.G
+    flop_unit = 4 * ((rows + 31) // 32 * 32) * wl.P * wl.D   # QK^T + PV MFMA work per (group, page)
+    comp_flops = n_units * flop_unit
+    attn_avg_s = float(attn_ms.mean()) * 1e-3
+    mfma_tflops = comp_flops / attn_avg_s / 1e12
+    gbs = alg_bytes / attn_avg_s / 1e9
+    traffic = recorded_traffic("hbm_bytes_per_launch")
+    roof = {"bound": "mfma", "achieved": mfma_tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": mfma_tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic,
+            "kernel": "union_attn_kernel<128,1>", "flops_per_unit": flop_unit,
+            "units_per_launch": n_units,
+            "hbm_definition": {"algorithmic_bytes": alg_bytes, "achieved_GBs": gbs,
+                               "peak_GBs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS}}
+
+    arms = {}
+    if not args.no_arms:
+        ident = torch.arange(wl.T, dtype=torch.int32, device="cuda").repeat(wl.H_kv, 1).contiguous()
+        for name, g_arm, ids_arm in [("identity_union8", wl.g, ident), ("per_query_g1", 1, ident)]:
+            n = 5 if g_arm == 1 else 10
+            for _ in range(2):
+                pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"],
+                                      dev["scales"], dev["sel_pages"], ids_arm, g_arm, O=O)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            for _ in range(n):
+                pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"],
+                                      dev["scales"], dev["sel_pages"], ids_arm, g_arm, O=O)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b) / n
+            us = union_stats(inp["sel_pages"], ids_arm.cpu().numpy(), g_arm, wl.N)
+            arms[name] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12,
+                          "union_pages_mean": float(us.mean()), "union_pages_total": int(us.sum())}
+        arms["regroup_gain_vs_identity"] = arms["identity_union8"]["ms"] / ms_per_step
+
+    cpu = None
+    if not args.no_cpu:
+        t0 = time.time()
+        cpu = cpu_baseline(inp, wl, args.cpu_seconds)
+        log(f"[bench] cpu baseline {time.time() - t0:.1f}s")
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded captures, Q/K/V ~ N(0,1), e4m3fn KV with per-page scales)",
+        "config": {"workload": wl.name, "tokens": wl.T, "H_q": wl.H_q, "H_kv": wl.H_kv,
+                   "head_dim": wl.D, "page": wl.P, "selected_pages": wl.S, "W": wl.W, "g": wl.g,
+                   "kv": "fp8_e4m3fn", "grouping": "regrouped"},
+        "latency_ms": {"complete_call": ms_per_step, "search_mean": float(search_ms.mean()),
+                       "attention_mean": float(attn_ms.mean()),
+                       "attention_median": float(np.median(attn_ms)),
+                       "attention_p90": float(np.percentile(attn_ms, 90)),
+                       "complete_call_cold_median": float(np.median(cold)) if cold else None},
+        "useful_flops": F_u,
+        "union": {"pages_mean": float(usz.mean()), "pages_max": int(usz.max()),
+                  "efficiency_useful_over_computed": F_u / comp_flops},
+        "roofline": roof, "arms": arms, "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,191 @@
+/*
+ * pageweaver.h -- C ABI of the query-union sparse-attention prefill path over
+ * a paged FP8 KV cache, for AMD Instinct MI355X (gfx950) only.
+ *
+ * Sources (cited by title and section):
+ *   [abs]   "PageWeaver: KV-Guided Query Unions for Sparse Attention",
+ *           arXiv 2610.11201, Abstract.
+ *   [radio] AI Radio episode "PageWeaver: KV-Guided Query Unions for Sparse
+ *           Attention", sections "Paper summary" and "Conclusion".
+ *
+ * The path has two calls that together form one complete call [abs: the
+ * speedups are quoted on the complete call, search plus attention]:
+ *   pw_group            a bounded search that only produces query IDs;
+ *   pw_union_attention  an ID-aware attention that reads Q rows by ID, loads
+ *                       each group's union of selected pages once and gives
+ *                       every query its own full attention over exactly its
+ *                       own selected pages (no reordered Q, no cross-page
+ *                       partial outputs) [abs].
+ * A third call, pw_dense_union_ref, is the direct KV-page union design study
+ * [abs; radio "Paper summary": disjoint page pairs, full membership, common
+ * and exclusive query lists] and produces the same O through per-pair partial
+ * outputs and a merge.
+ *
+ * Conventions for every call:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller; the
+ *     library keeps no reference after the call is enqueued.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns without synchronising.
+ *   - The library allocates no device memory; scratch space comes from the
+ *     caller's workspace (`ws`, `ws_bytes`), sized by the matching
+ *     *_workspace_bytes() query.  A call whose query returns 0 accepts
+ *     ws = NULL.
+ *   - Problems that can be checked on the host are reported before anything
+ *     is enqueued, through the returned status; pw_last_error() then holds a
+ *     message for the calling thread.  A HIP launch failure returns
+ *     PW_ERR_HIP.  No call aborts, throws or prints.
+ *   - Calls are re-entrant: there is no global mutable state besides the
+ *     thread-local error message.
+ *
+ * Shapes (pw_shape):
+ *   T        tokens of the prefilled context = number of queries; query t is
+ *            at token t and sees key j iff j <= t (whole-context causal
+ *            prefill).
+ *   H_q,H_kv query and KV heads; G = H_q / H_kv; Q head hq reads KV head
+ *            hq / G.
+ *   D        head dimension (64 or 128).
+ *   P        page size in tokens (16, 32 or 64); key j lives in page j / P,
+ *            slot j % P.
+ *   N_pages  pages of the cache; T == N_pages * P.
+ *   S        selected-page slots per (KV head, query).
+ *
+ * Tensor layouts (row-major, innermost last):
+ *   sel_pages int32 [H_kv][T][S]     selected pages of each (KV head, query).
+ *             A slot outside [0, N_pages) is empty; repeated pages count
+ *             once (the support is a set); order does not matter.
+ *   query_ids int32 [H_kv][T]        per KV head, a permutation of 0..T-1;
+ *             group k of that head is entries [k*g, k*g + g).
+ *   Q         bf16  [T][H_q][D]      (bit patterns as uint16).
+ *   K_fp8     e4m3fn [N_pages][H_kv][P][D]   token-major pages.
+ *   V_fp8     e4m3fn [N_pages][H_kv][D][P]   dim-major pages: the token,
+ *             which PV contracts over, is the contiguous index.
+ *   scales    fp32  [2][N_pages][H_kv]        K scale then V scale of each
+ *             (page, KV head); the value of a code is e4m3fn(code) * scale.
+ *             Scales must be positive and finite.
+ *   O         bf16  [T][H_q][D]      output, one writer per row.
+ *
+ * e4m3fn is the OCP 8-bit E4M3 format with a NaN and no infinities (max 448).
+ */
+#ifndef PAGEWEAVER_H
+#define PAGEWEAVER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pw_status {
+  PW_OK = 0,
+  PW_ERR_NULL = -1,        /* a required pointer is NULL                     */
+  PW_ERR_DIMS = -2,        /* inconsistent or non-positive dimensions        */
+  PW_ERR_UNSUPPORTED = -3, /* valid but outside the compiled support set     */
+  PW_ERR_WORKSPACE = -4,   /* workspace smaller than *_workspace_bytes()     */
+  PW_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed     */
+} pw_status;
+
+typedef struct pw_shape {
+  int32_t T, H_q, H_kv, D, P, N_pages, S;
+} pw_shape;
+
+/* ---------------------------------------------------------------------------
+ * pw_group -- bounded-window greedy grouping; produces query IDs only.
+ *
+ * [abs]: a bounded GPU search produces query IDs.  [radio "Paper summary"]:
+ * within a bounded window W the members of a query-owned group are collected
+ * greedily, taking queries whose selected sets add few new pages; the group
+ * size g is fixed independently of W.
+ *
+ * For every KV head h and every aligned window of W consecutive query IDs
+ * [w*W, min(T, (w+1)*W)): repeatedly, the lowest unassigned ID seeds a group
+ * whose union U starts as its support; then, until the group has g members or
+ * the window is exhausted, the unassigned query c minimising
+ * (|support(c) \ U| in pages, c) joins and U grows by its support.  IDs are
+ * written window by window, group by group, members in insertion order.  The
+ * result is unique, so it is bit-exact against any correct implementation.
+ *
+ * In : sel_pages (see layouts), W in [1, 256], g in [1, 8].
+ * Out: query_ids int32 [H_kv][T] (every entry written).
+ * Support set: N_pages <= 1024.  Workspace: none (returns 0).
+ * ------------------------------------------------------------------------- */
+size_t pw_group_workspace_bytes(const pw_shape* shape, int32_t W, int32_t g);
+pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W,
+                   int32_t g, int32_t* query_ids, void* ws, size_t ws_bytes,
+                   void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pw_union_attention -- ID-aware union attention.
+ *
+ * [abs]: query unions share page loads and fill matrix-core tiles; each query
+ * keeps its original support and sole ownership of its output; the kernel
+ * consumes the IDs without a reordered Q tensor and without cross-page
+ * partial outputs.
+ *
+ * For each KV head h and group k (entries [k*g, k*g+g) of query_ids[h]), the
+ * union of the members' selected pages is loaded once, in ascending page
+ * order; every member t and each of its G Q heads hq computes
+ *   O[t][hq] = sum_j softmax_j(<Q[t][hq], Khat_j> / sqrt(D)) Vhat_j
+ * over exactly the keys j of its own selected pages with j <= t
+ * (Khat/Vhat = e4m3fn(code) * scale).  O[t][hq] = 0 when that key set is
+ * empty.  Arithmetic: bf16 x bf16 products with fp32 accumulation (the e4m3fn
+ * codes convert to bf16 exactly), fp32 online softmax, bf16 (RNE) output.
+ * The result of a row does not depend on which other queries share its group.
+ *
+ * In : Q, K_fp8, V_fp8, scales, sel_pages, query_ids (see layouts), g in
+ *      [1, 8] with g * G <= 64.  IDs outside [0, T) are skipped; a
+ *      query_ids row that is not a permutation leaves unlisted rows of O
+ *      unwritten.
+ * Out: O.
+ * Support set: D in {64, 128}; P in {16, 32, 64}; N_pages <= 32768.
+ * Workspace: none (returns 0).
+ * ------------------------------------------------------------------------- */
+size_t pw_union_attention_workspace_bytes(const pw_shape* shape, int32_t g);
+pw_status pw_union_attention(const pw_shape* shape, const uint16_t* Q,
+                             const uint8_t* K_fp8, const uint8_t* V_fp8,
+                             const float* scales, const int32_t* sel_pages,
+                             const int32_t* query_ids, int32_t g, uint16_t* O,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pw_dense_union_ref -- direct KV-page union (design-study comparison).
+ *
+ * [abs]: a direct KV-page union implementation studies non-local reuse
+ * against reduction cost.  [radio "Paper summary"]: it uses disjoint page
+ * pairs and the full membership of each page to form common or exclusive
+ * query lists.
+ *
+ * Pages are paired as (2k, 2k+1).  Per KV head, the full membership of each
+ * pair (every query that selected either page) is built on the device; each
+ * (query, pair) computes a partial (running max, sum, unnormalised output)
+ * over its own visible keys in the pair (both pages for the common list, one
+ * page for an exclusive list), written to the workspace; a second pass merges
+ * each query's partials by log-sum-exp into O.  Same O as
+ * pw_union_attention up to floating-point order.
+ *
+ * In/Out/support: as pw_union_attention (no query_ids); queries are processed
+ * in chunks sized so that the workspace stays bounded.
+ * Workspace: pw_dense_union_ref_workspace_bytes(shape) bytes, 256-byte
+ * aligned.
+ * ------------------------------------------------------------------------- */
+size_t pw_dense_union_ref_workspace_bytes(const pw_shape* shape);
+pw_status pw_dense_union_ref(const pw_shape* shape, const uint16_t* Q,
+                             const uint8_t* K_fp8, const uint8_t* V_fp8,
+                             const float* scales, const int32_t* sel_pages,
+                             uint16_t* O, void* ws, size_t ws_bytes,
+                             void* stream);
+
+/* Static description of a status code. */
+const char* pw_status_string(pw_status status);
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* pw_last_error(void);
+/* ABI version of this header, PW_ABI_VERSION. */
+int32_t pw_abi_version(void);
+
+#define PW_ABI_VERSION 1
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEWEAVER_H */

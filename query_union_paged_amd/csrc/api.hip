@@ -1,0 +1,136 @@
+// extern "C" entry points of libpageweaver: host-side validation, then the
+// launches on the caller's stream.  Declarations and contracts live in
+// include/pageweaver.h.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "pw_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+pw_status fail(pw_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+pw_status ok() {
+  g_last_error[0] = '\0';
+  return PW_OK;
+}
+
+pw_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(PW_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Checks shared by every call: consistent, positive dimensions.
+pw_status check_shape(const pw_shape* s) {
+  if (!s) return fail(PW_ERR_NULL, "shape is NULL");
+  if (s->T <= 0 || s->H_q <= 0 || s->H_kv <= 0 || s->D <= 0 || s->P <= 0 || s->N_pages <= 0 ||
+      s->S <= 0)
+    return fail(PW_ERR_DIMS, "all dimensions must be positive (T=%d H_q=%d H_kv=%d D=%d P=%d N=%d S=%d)",
+                s->T, s->H_q, s->H_kv, s->D, s->P, s->N_pages, s->S);
+  if ((int64_t)s->N_pages * s->P != s->T)
+    return fail(PW_ERR_DIMS, "T (%d) must equal N_pages * P (%d * %d)", s->T, s->N_pages, s->P);
+  if (s->H_q % s->H_kv != 0)
+    return fail(PW_ERR_DIMS, "H_q (%d) must be a multiple of H_kv (%d)", s->H_q, s->H_kv);
+  return PW_OK;
+}
+
+pw_status check_attention_support(const pw_shape* s, int g) {
+  const int G = s->H_q / s->H_kv;
+  if (g < 1 || g > 8) return fail(PW_ERR_UNSUPPORTED, "g = %d outside [1, 8]", g);
+  if (g * G > 64) return fail(PW_ERR_UNSUPPORTED, "g * G = %d exceeds 64 query rows", g * G);
+  if (s->D != 64 && s->D != 128) return fail(PW_ERR_UNSUPPORTED, "D = %d not in {64, 128}", s->D);
+  if (s->P != 16 && s->P != 32 && s->P != 64)
+    return fail(PW_ERR_UNSUPPORTED, "P = %d not in {16, 32, 64}", s->P);
+  if (s->N_pages > 32768) return fail(PW_ERR_UNSUPPORTED, "N_pages = %d exceeds 32768", s->N_pages);
+  if (g * s->S > 1024) return fail(PW_ERR_UNSUPPORTED, "g * S = %d exceeds 1024", g * s->S);
+  return PW_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pw_status_string(pw_status st) {
+  switch (st) {
+    case PW_OK: return "ok";
+    case PW_ERR_NULL: return "null pointer";
+    case PW_ERR_DIMS: return "invalid dimensions";
+    case PW_ERR_UNSUPPORTED: return "unsupported configuration";
+    case PW_ERR_WORKSPACE: return "workspace too small";
+    case PW_ERR_HIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+const char* pw_last_error(void) { return g_last_error; }
+
+int32_t pw_abi_version(void) { return PW_ABI_VERSION; }
+
+size_t pw_group_workspace_bytes(const pw_shape*, int32_t, int32_t) { return 0; }
+
+pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W, int32_t g,
+                   int32_t* query_ids, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  pw_status st = check_shape(shape);
+  if (st != PW_OK) return st;
+  if (!sel_pages || !query_ids) return fail(PW_ERR_NULL, "sel_pages and query_ids are required");
+  if (W < 1 || W > 256) return fail(PW_ERR_UNSUPPORTED, "W = %d outside [1, 256]", W);
+  if (g < 1 || g > 8) return fail(PW_ERR_UNSUPPORTED, "g = %d outside [1, 8]", g);
+  if (shape->N_pages > 1024)
+    return fail(PW_ERR_UNSUPPORTED, "N_pages = %d exceeds 1024 for the search", shape->N_pages);
+  return hip_status(pw::launch_group(*shape, sel_pages, W, g, query_ids, (hipStream_t)stream),
+                    "pw_group launch");
+}
+
+size_t pw_union_attention_workspace_bytes(const pw_shape*, int32_t) { return 0; }
+
+pw_status pw_union_attention(const pw_shape* shape, const uint16_t* Q, const uint8_t* K_fp8,
+                             const uint8_t* V_fp8, const float* scales, const int32_t* sel_pages,
+                             const int32_t* query_ids, int32_t g, uint16_t* O, void* ws,
+                             size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  pw_status st = check_shape(shape);
+  if (st != PW_OK) return st;
+  if (!Q || !K_fp8 || !V_fp8 || !scales || !sel_pages || !query_ids || !O)
+    return fail(PW_ERR_NULL, "Q, K_fp8, V_fp8, scales, sel_pages, query_ids and O are required");
+  st = check_attention_support(shape, g);
+  if (st != PW_OK) return st;
+  return hip_status(pw::launch_union_attention(*shape, Q, K_fp8, V_fp8, scales, sel_pages,
+                                               query_ids, g, O, (hipStream_t)stream),
+                    "pw_union_attention launch");
+}
+
+size_t pw_dense_union_ref_workspace_bytes(const pw_shape* shape) {
+  if (check_shape(shape) != PW_OK) return 0;
+  return pw::dense_union_workspace(*shape);
+}
+
+pw_status pw_dense_union_ref(const pw_shape* shape, const uint16_t* Q, const uint8_t* K_fp8,
+                             const uint8_t* V_fp8, const float* scales, const int32_t* sel_pages,
+                             uint16_t* O, void* ws, size_t ws_bytes, void* stream) {
+  pw_status st = check_shape(shape);
+  if (st != PW_OK) return st;
+  if (!Q || !K_fp8 || !V_fp8 || !scales || !sel_pages || !O)
+    return fail(PW_ERR_NULL, "Q, K_fp8, V_fp8, scales, sel_pages and O are required");
+  st = check_attention_support(shape, 1);
+  if (st != PW_OK) return st;
+  const size_t need = pw::dense_union_workspace(*shape);
+  if (need > 0 && !ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
+  if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (((uintptr_t)ws & 255) != 0) return fail(PW_ERR_DIMS, "workspace must be 256-byte aligned");
+  return hip_status(pw::launch_dense_union(*shape, Q, K_fp8, V_fp8, scales, sel_pages, O, ws,
+                                           ws_bytes, (hipStream_t)stream),
+                    "pw_dense_union_ref launch");
+}
+
+}  // extern "C"

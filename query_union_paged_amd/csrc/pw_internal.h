@@ -1,0 +1,62 @@
+// Internal declarations shared by the HIP sources of libpageweaver (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pageweaver.h"
+
+namespace pw {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+
+constexpr int kWave = 64;
+
+// Make this wave's earlier LDS writes visible to its later LDS reads (the
+// lanes of one wave exchange data through LDS without a workgroup barrier).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, off));
+  return v;
+}
+
+__device__ __forceinline__ int lane_prefix(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
+}
+
+// Eight e4m3fn bytes (two dwords) -> eight bf16, exactly (every e4m3fn value,
+// subnormals included, is a bf16 value).
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// Host-side launchers (implemented next to their kernels).
+hipError_t launch_group(const pw_shape& s, const int32_t* sel, int W, int g, int32_t* ids,
+                        hipStream_t stream);
+hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
+                                  const uint8_t* V, const float* scales, const int32_t* sel,
+                                  const int32_t* ids, int g, uint16_t* O, hipStream_t stream);
+size_t dense_union_workspace(const pw_shape& s);
+hipError_t launch_dense_union(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
+                              const uint8_t* V, const float* scales, const int32_t* sel,
+                              uint16_t* O, void* ws, size_t ws_bytes, hipStream_t stream);
+
+}  // namespace pw

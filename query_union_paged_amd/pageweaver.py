@@ -1,0 +1,165 @@
+"""Thin ctypes binding of libpageweaver (argument marshalling only).
+
+Every step of the path runs in the HIP kernels behind the C ABI declared in
+include/pageweaver.h; this module only checks tensor dtypes, shapes and
+devices, passes raw device pointers and the current HIP stream, and turns a
+non-OK status into an exception.  Importing it fails loudly when the library
+has not been built: there is no fallback of any kind.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpageweaver.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pageweaver.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m query_union_paged_amd.build` "
+        "(hipcc, gfx950). The path has no CPU or PyTorch fallback.")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+PW_OK, PW_ERR_NULL, PW_ERR_DIMS, PW_ERR_UNSUPPORTED, PW_ERR_WORKSPACE, PW_ERR_HIP = 0, -1, -2, -3, -4, -5
+
+
+class PWShape(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "H_q", "H_kv", "D", "P", "N_pages", "S")]
+
+
+class PWError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        detail = _lib.pw_last_error().decode()
+        super().__init__(f"{where}: {_lib.pw_status_string(status).decode()} ({status}): {detail}")
+
+
+_vp, _sz, _i32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+_SHP = ctypes.POINTER(PWShape)
+_SIGS = {
+    "pw_group_workspace_bytes": (_sz, [_SHP, _i32, _i32]),
+    "pw_group": (_i32, [_SHP, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "pw_union_attention_workspace_bytes": (_sz, [_SHP, _i32]),
+    "pw_union_attention": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "pw_dense_union_ref_workspace_bytes": (_sz, [_SHP]),
+    "pw_dense_union_ref": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pw_status_string": (ctypes.c_char_p, [_i32]),
+    "pw_last_error": (ctypes.c_char_p, []),
+    "pw_abi_version": (_i32, []),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype, _fn.argtypes = _res, _args
+
+
+def header_functions():
+    """Names of the functions include/pageweaver.h declares."""
+    text = open(HEADER_PATH).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(pw_\w+)\s*\(", text, re.M)))
+
+
+def shape(T, H_q, H_kv, D, P, N_pages, S) -> PWShape:
+    return PWShape(T, H_q, H_kv, D, P, N_pages, S)
+
+
+def shape_of(q: torch.Tensor, k_fp8: torch.Tensor, sel_pages: torch.Tensor) -> PWShape:
+    T, H_q, D = q.shape
+    N, H_kv, P, _ = k_fp8.shape
+    return PWShape(T, H_q, H_kv, D, P, N, sel_pages.shape[2])
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, shape_=None) -> int:
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a device tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape_ is not None and tuple(t.shape) != tuple(shape_):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape_)}")
+    return t.data_ptr()
+
+
+_U8 = (torch.uint8, torch.float8_e4m3fn)
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _check(status: int, where: str):
+    if status != PW_OK:
+        raise PWError(status, where)
+
+
+def pw_group(shp: PWShape, sel_pages: torch.Tensor, W: int, g: int,
+             query_ids: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    sel = _dev(sel_pages, "sel_pages", (torch.int32,), (shp.H_kv, shp.T, shp.S))
+    if query_ids is None:
+        query_ids = torch.empty((shp.H_kv, shp.T), dtype=torch.int32, device=sel_pages.device)
+    ids = _dev(query_ids, "query_ids", (torch.int32,), (shp.H_kv, shp.T))
+    _check(_lib.pw_group(ctypes.byref(shp), sel, W, g, ids, None, 0, _stream(stream)), "pw_group")
+    return query_ids
+
+
+def pw_union_attention(shp: PWShape, Q, K_fp8, V_fp8, scales, sel_pages, query_ids, g: int,
+                       O: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    T, Hq, Hkv, D, P, N, S = shp.T, shp.H_q, shp.H_kv, shp.D, shp.P, shp.N_pages, shp.S
+    q = _dev(Q, "Q", _BF16, (T, Hq, D))
+    k = _dev(K_fp8, "K_fp8", _U8, (N, Hkv, P, D))
+    v = _dev(V_fp8, "V_fp8", _U8, (N, Hkv, D, P))
+    sc = _dev(scales, "scales", (torch.float32,), (2, N, Hkv))
+    sel = _dev(sel_pages, "sel_pages", (torch.int32,), (Hkv, T, S))
+    ids = _dev(query_ids, "query_ids", (torch.int32,), (Hkv, T))
+    if O is None:
+        O = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=Q.device)
+    o = _dev(O, "O", _BF16, (T, Hq, D))
+    _check(_lib.pw_union_attention(ctypes.byref(shp), q, k, v, sc, sel, ids, g, o, None, 0,
+                                   _stream(stream)), "pw_union_attention")
+    return O
+
+
+def pw_dense_union_ref_workspace_bytes(shp: PWShape) -> int:
+    return int(_lib.pw_dense_union_ref_workspace_bytes(ctypes.byref(shp)))
+
+
+def pw_dense_union_ref(shp: PWShape, Q, K_fp8, V_fp8, scales, sel_pages,
+                       O: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
+    T, Hq, Hkv, D, P, N, S = shp.T, shp.H_q, shp.H_kv, shp.D, shp.P, shp.N_pages, shp.S
+    q = _dev(Q, "Q", _BF16, (T, Hq, D))
+    k = _dev(K_fp8, "K_fp8", _U8, (N, Hkv, P, D))
+    v = _dev(V_fp8, "V_fp8", _U8, (N, Hkv, D, P))
+    sc = _dev(scales, "scales", (torch.float32,), (2, N, Hkv))
+    sel = _dev(sel_pages, "sel_pages", (torch.int32,), (Hkv, T, S))
+    if O is None:
+        O = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=Q.device)
+    o = _dev(O, "O", _BF16, (T, Hq, D))
+    need = pw_dense_union_ref_workspace_bytes(shp)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
+    ws, nbytes = (0, 0) if workspace is None else (_dev(workspace, "workspace", (torch.uint8,)), workspace.numel())
+    _check(_lib.pw_dense_union_ref(ctypes.byref(shp), q, k, v, sc, sel, o, ws or None, nbytes,
+                                   _stream(stream)), "pw_dense_union_ref")
+    return O
+
+
+def to_device(inputs: dict, device="cuda") -> dict:
+    """Upload generator output (numpy, C-ABI layouts) as device tensors."""
+    out = {}
+    for key, arr in inputs.items():
+        if key == "q_bits":
+            t = torch.from_numpy(arr.view("int16")).view(torch.bfloat16)
+        else:
+            t = torch.from_numpy(arr)
+        out[key] = t.to(device).contiguous()
+    return out

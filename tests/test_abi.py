@@ -1,0 +1,92 @@
+"""The C-ABI library loads, exports every declared symbol and validates on the host.
+
+CPU only: every call here returns its status before any HIP call is made.
+"""
+import ctypes
+import os
+import subprocess
+
+import pytest
+
+from query_union_paged_amd import pageweaver as pw
+
+FAKE = ctypes.c_void_p(0x1000)   # never dereferenced: each call below fails validation first
+
+
+def test_every_declared_symbol_is_exported():
+    names = pw.header_functions()
+    assert {"pw_group", "pw_union_attention", "pw_dense_union_ref"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", pw.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert pw._lib.pw_abi_version() == 1
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4, -5):
+        assert pw._lib.pw_status_string(st).decode()
+    assert pw._lib.pw_status_string(42) == b"unknown status"
+
+
+def _shape(**kw):
+    base = dict(T=1024, H_q=4, H_kv=1, D=64, P=16, N_pages=64, S=8)
+    base.update(kw)
+    return pw.PWShape(*[base[k] for k in ("T", "H_q", "H_kv", "D", "P", "N_pages", "S")])
+
+
+def _group(shp, W=32, g=8, sel=FAKE, ids=FAKE):
+    return pw._lib.pw_group(ctypes.byref(shp), sel, W, g, ids, None, 0, None)
+
+
+def _attn(shp, g=8, ptrs=None):
+    p = ptrs or [FAKE] * 7
+    return pw._lib.pw_union_attention(ctypes.byref(shp), p[0], p[1], p[2], p[3], p[4], p[5], g,
+                                      p[6], None, 0, None)
+
+
+def test_group_validation():
+    assert pw._lib.pw_group(None, FAKE, 32, 8, FAKE, None, 0, None) == pw.PW_ERR_NULL
+    assert _group(_shape(T=0)) == pw.PW_ERR_DIMS
+    assert _group(_shape(T=1000)) == pw.PW_ERR_DIMS                 # T != N_pages * P
+    assert _group(_shape(H_q=6, H_kv=4)) == pw.PW_ERR_DIMS
+    assert _group(_shape(), sel=None) == pw.PW_ERR_NULL
+    assert _group(_shape(), ids=None) == pw.PW_ERR_NULL
+    assert _group(_shape(), W=0) == pw.PW_ERR_UNSUPPORTED
+    assert _group(_shape(), W=257) == pw.PW_ERR_UNSUPPORTED
+    assert _group(_shape(), g=9) == pw.PW_ERR_UNSUPPORTED
+    assert _group(_shape(T=2048 * 16, N_pages=2048)) == pw.PW_ERR_UNSUPPORTED
+    assert b"W = 257" in (_group(_shape(), W=257) and pw._lib.pw_last_error())
+    assert pw._lib.pw_group_workspace_bytes(ctypes.byref(_shape()), 32, 8) == 0
+
+
+def test_attention_validation():
+    assert _attn(_shape(), ptrs=[FAKE, None] + [FAKE] * 5) == pw.PW_ERR_NULL
+    assert _attn(_shape(), ptrs=[FAKE] * 6 + [None]) == pw.PW_ERR_NULL
+    assert _attn(_shape(D=96)) == pw.PW_ERR_UNSUPPORTED
+    assert _attn(_shape(P=8, N_pages=128)) == pw.PW_ERR_UNSUPPORTED
+    assert _attn(_shape(), g=0) == pw.PW_ERR_UNSUPPORTED
+    assert _attn(_shape(H_q=16, H_kv=1), g=8) == pw.PW_ERR_UNSUPPORTED   # 128 query rows
+    assert _attn(_shape(S=200), g=8) == pw.PW_ERR_UNSUPPORTED           # g * S > 1024
+    assert _attn(_shape(N_pages=65536, T=65536 * 16)) == pw.PW_ERR_UNSUPPORTED
+    assert _attn(_shape(S=-1)) == pw.PW_ERR_DIMS
+    assert pw._lib.pw_union_attention_workspace_bytes(ctypes.byref(_shape()), 8) == 0
+
+
+def test_dense_union_validation():
+    shp = _shape()
+    f = pw._lib.pw_dense_union_ref
+    assert f(ctypes.byref(shp), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == pw.PW_ERR_NULL
+    assert f(ctypes.byref(_shape(D=80)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == pw.PW_ERR_UNSUPPORTED
+    need = pw._lib.pw_dense_union_ref_workspace_bytes(ctypes.byref(shp))
+    if need > 0:
+        assert f(ctypes.byref(shp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == pw.PW_ERR_WORKSPACE
+        assert f(ctypes.byref(shp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None) == pw.PW_ERR_NULL
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    shp = _shape()
+    with pytest.raises(TypeError):
+        pw.pw_group(shp, torch.zeros((1, 1024, 8), dtype=torch.int32), 32, 8)

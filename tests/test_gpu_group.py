@@ -1,0 +1,90 @@
+"""pw_group on the GPU against the CPU greedy oracle: bit-exact query IDs."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+from query_union_paged_amd import synth
+from oracle.greedy import group_ids
+from tests.gpu_common import WORKERS, host_inputs, log
+from tests.oracle_helpers import tiny_problem
+
+pytestmark = pytest.mark.gpu
+
+
+def _pw():
+    from query_union_paged_amd import pageweaver
+    return pageweaver
+
+
+def _gpu_ids(sel_np, N, P, W, g, H_q=None, D=128):
+    pw = _pw()
+    H, T, S = sel_np.shape
+    shp = pw.shape(T, H_q or H, H, D, P, N, S)
+    sel = torch.from_numpy(sel_np).cuda()
+    ids = pw.pw_group(shp, sel, W, g)
+    torch.cuda.synchronize()
+    return ids.cpu().numpy()
+
+
+@pytest.mark.parametrize("name", synth.WORKLOAD_ORDER)
+def test_group_ids_bit_exact(name):
+    wl = synth.WORKLOADS[name]
+    log(f"[case] pw_group {name} W={wl.W} g={wl.g}")
+    sel = host_inputs(name)["sel_pages"]
+    got = _gpu_ids(sel, wl.N, wl.P, wl.W, wl.g, wl.H_q, wl.D)
+    t0 = time.time()
+    ref = group_ids(sel, wl.N, wl.W, wl.g, workers=WORKERS)
+    log(f"[oracle] greedy {name}: {time.time() - t0:.1f}s on {WORKERS} processes")
+    assert np.array_equal(got, ref), f"{(got != ref).sum()} IDs differ"
+
+
+@pytest.mark.parametrize("W,g", [(32, 1), (32, 3), (64, 8), (96, 8), (128, 4), (256, 8), (200, 5), (256, 2)])
+def test_group_windows_and_sizes(W, g):
+    # random supports over N = 256 pages, including ragged last windows and groups
+    log(f"[case] pw_group random W={W} g={g}")
+    rng = np.random.default_rng(W * 10 + g)
+    T, P, S = 1024, 4, 12
+    N = T // P
+    sel = rng.integers(-3, N + 3, size=(2, T, S)).astype(np.int32)
+    sel[:, ::3] %= 20        # clustered rows: many equal-cost ties
+    got = _gpu_ids(sel, N, P, W, g)
+    ref = group_ids(sel, N, W, g, workers=WORKERS)
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("N", [64, 100, 1024])
+def test_group_page_counts(N):
+    log(f"[case] pw_group N={N}")
+    rng = np.random.default_rng(N)
+    P = 16
+    T = N * P
+    sel = rng.integers(0, N, size=(1, T, 6)).astype(np.int32)
+    got = _gpu_ids(sel, N, P, 64, 8)
+    ref = group_ids(sel, N, 64, 8, workers=WORKERS)
+    assert np.array_equal(got, ref)
+
+
+def test_group_golden_cases():
+    import json
+    import os
+    doc = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "greedy_cases.json")))
+    for case in doc["cases"]:
+        log(f"[case] pw_group golden {case['name']}")
+        sel = np.array(case["sel"], dtype=np.int32)
+        T, N, W, g = sel.shape[0], case["N"], case["W"], case["g"]
+        # The ABI needs T == N_pages * P.  Pad with empty queries only when the
+        # padding forms windows of its own, so the real windows are unchanged.
+        if T % N == 0:
+            n_abi, p_abi = N, T // N
+        elif T % W == 0 and N >= T:
+            n_abi, p_abi = N, 1
+        else:
+            assert sel.max() < T
+            n_abi, p_abi = T, 1
+        t_abi = n_abi * p_abi
+        full = np.full((1, t_abi, sel.shape[1]), -1, dtype=np.int32)
+        full[0, :T] = sel
+        got = _gpu_ids(full, n_abi, p_abi, W, g)
+        assert got[0, :T].tolist() == case["expected"], case["name"]

@@ -1,0 +1,149 @@
+"""pw_union_attention on the GPU against the fp64 oracle (element by element)."""
+import numpy as np
+import pytest
+import torch
+
+from query_union_paged_amd import synth
+from tests.gpu_common import (assert_close, gpu_rows, host_inputs, log, oracle_rows,
+                              sample_pairs)
+from tests.oracle_helpers import tiny_problem
+
+pytestmark = pytest.mark.gpu
+
+
+def _pw():
+    from query_union_paged_amd import pageweaver
+    return pageweaver
+
+
+def _run(inp_host, g, ids_mode="regroup", W=None):
+    """Upload, build IDs (GPU search, identity or given), run the union kernel."""
+    pw = _pw()
+    dev = pw.to_device(inp_host)
+    T, Hq, D = inp_host["q_bits"].shape
+    N, Hkv, P, _ = inp_host["k_codes"].shape
+    S = inp_host["sel_pages"].shape[2]
+    shp = pw.shape(T, Hq, Hkv, D, P, N, S)
+    if isinstance(ids_mode, np.ndarray):
+        ids = torch.from_numpy(ids_mode).cuda()
+    elif ids_mode == "regroup":
+        ids = pw.pw_group(shp, dev["sel_pages"], W, g)
+    else:
+        ids = torch.arange(T, dtype=torch.int32, device="cuda").repeat(Hkv, 1).contiguous()
+    O = pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
+                              dev["sel_pages"], ids, g)
+    torch.cuda.synchronize()
+    return O, ids
+
+
+def _all_pairs(Hkv, T):
+    return [(h, t) for h in range(Hkv) for t in range(T)]
+
+
+@pytest.mark.parametrize("variant,peaked", [(0, False), (1, False), (2, False), (0, True)])
+@pytest.mark.parametrize("arm", ["regroup", "identity", "g1"])
+def test_tiny_full(variant, peaked, arm):
+    wl = synth.WORKLOADS["tiny_1k"]
+    log(f"[case] union tiny_1k v{variant} peaked={peaked} arm={arm}")
+    inp = host_inputs("tiny_1k", variant, peaked)
+    g = 1 if arm == "g1" else wl.g
+    O, _ = _run(inp, g, "identity" if arm == "identity" else "regroup", wl.W)
+    pairs = _all_pairs(wl.H_kv, wl.T)
+    assert_close(gpu_rows(O, pairs, wl.G), oracle_rows(inp, pairs), f"tiny v{variant} {arm}")
+
+
+def test_8k_full_and_arm_identity():
+    wl = synth.WORKLOADS["prefill_8k"]
+    log("[case] union prefill_8k full")
+    inp = host_inputs("prefill_8k")
+    O_r, ids = _run(inp, wl.g, "regroup", wl.W)
+    pairs = _all_pairs(wl.H_kv, wl.T)
+    ref = oracle_rows(inp, pairs)
+    assert_close(gpu_rows(O_r, pairs, wl.G), ref, "8k regroup")
+    O_i, _ = _run(inp, wl.g, "identity")
+    # a row's result does not depend on the group it sits in
+    same = (O_r.float() == O_i.float()).float().mean().item()
+    log(f"[parity] 8k regroup vs identity: fraction of equal elements {same:.6f}")
+    assert same == 1.0
+    O_1, _ = _run(inp, 1, "identity")
+    assert (O_1.float() == O_r.float()).all()
+    # run-to-run determinism
+    O_r2, ids2 = _run(inp, wl.g, "regroup", wl.W)
+    assert torch.equal(ids, ids2) and torch.equal(O_r.view(torch.int16), O_r2.view(torch.int16))
+
+
+def test_8k_peaked_sampled():
+    wl = synth.WORKLOADS["prefill_8k"]
+    log("[case] union prefill_8k peaked")
+    inp = host_inputs("prefill_8k", 0, True)
+    O, _ = _run(inp, wl.g, "regroup", wl.W)
+    pairs = sample_pairs(wl)
+    assert_close(gpu_rows(O, pairs, wl.G), oracle_rows(inp, pairs), "8k peaked")
+
+
+@pytest.mark.parametrize("name,arms", [("prefill_32k", ["regroup", "identity"]),
+                                       ("prefill_64k", ["regroup", "identity", "g1"]),
+                                       ("prefill_64k_70b", ["regroup", "identity"])])
+def test_large_sampled(name, arms):
+    wl = synth.WORKLOADS[name]
+    inp = host_inputs(name)
+    pairs = sample_pairs(wl)
+    ref = oracle_rows(inp, pairs)
+    for arm in arms:
+        log(f"[case] union {name} arm={arm}")
+        g = 1 if arm == "g1" else wl.g
+        O, _ = _run(inp, g, "identity" if arm == "identity" else "regroup", wl.W)
+        assert_close(gpu_rows(O, pairs, wl.G), ref, f"{name} {arm}")
+        del O
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("D,P,Hq,Hkv,S,g", [
+    (64, 16, 4, 1, 8, 8), (64, 32, 8, 2, 5, 8), (128, 64, 8, 1, 4, 8),   # G = 8: two row tiles
+    (128, 16, 2, 2, 6, 8), (64, 64, 16, 2, 3, 4), (128, 32, 4, 2, 7, 3),  # g = 3: ragged last group
+    (128, 64, 1, 1, 5, 8), (64, 16, 8, 4, 9, 5), (128, 64, 32, 1, 3, 2)])
+def test_shapes_and_group_sizes(D, P, Hq, Hkv, S, g):
+    log(f"[case] union shape D={D} P={P} Hq={Hq} Hkv={Hkv} S={S} g={g}")
+    T = 16 * P
+    inp = tiny_problem(T=T, Hq=Hq, Hkv=Hkv, D=D, P=P, S=S, seed=D + P + S + g)
+    rng = np.random.default_rng(g)
+    ids = np.stack([rng.permutation(T) for _ in range(Hkv)]).astype(np.int32)
+    O, _ = _run(inp, g, ids)
+    pairs = _all_pairs(Hkv, T)
+    assert_close(gpu_rows(O, pairs, Hq // Hkv), oracle_rows(inp, pairs), f"shape D{D} P{P} g{g}")
+
+
+def test_edge_cases_in_selection():
+    # empty supports, repeats, out-of-range slots and pages in the causal future
+    log("[case] union selection edge cases")
+    T, P, S = 512, 16, 6
+    inp = tiny_problem(T=T, Hq=8, Hkv=2, D=128, P=P, S=S, seed=77)
+    sel = inp["sel_pages"].copy()
+    sel[0, 100] = -1                         # empty support -> O = 0
+    sel[1, 7] = [40, 31, -1, 99, -7, 31]     # only future / out-of-range pages -> O = 0
+    sel[0, 300] = [18, 18, 0, 0, 31, -1]     # repeats and one future page
+    sel[1, 511] = [31, 0, 31, 5, 5, 2]
+    inp = dict(inp, sel_pages=sel)
+    O, _ = _run(inp, 8, "regroup", 64)
+    pairs = _all_pairs(2, T)
+    got = gpu_rows(O, pairs, 4)
+    ref = oracle_rows(inp, pairs)
+    assert_close(got, ref, "edge cases")
+    o = O.float().cpu().numpy()
+    assert np.all(o[100, 0:4] == 0) and np.all(o[7, 4:8] == 0)
+
+
+def test_invalid_arguments_raise():
+    pw = _pw()
+    inp = tiny_problem(T=64, Hq=4, Hkv=1, D=64, P=16, S=2, seed=1)
+    dev = pw.to_device(inp)
+    shp = pw.shape(64, 4, 1, 64, 16, 4, 2)
+    ids = torch.arange(64, dtype=torch.int32, device="cuda")[None].contiguous()
+    with pytest.raises(pw.PWError) as e:
+        pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
+                              dev["sel_pages"], ids, 9)
+    assert e.value.status == pw.PW_ERR_UNSUPPORTED
+    bad = pw.shape(64, 4, 1, 64, 16, 5, 2)
+    with pytest.raises((pw.PWError, ValueError)):
+        pw.pw_union_attention(bad, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
+                              dev["sel_pages"], ids, 8)
