@@ -76,25 +76,32 @@ def recorded_traffic(per_launch_key: str):
 
 def cpu_baseline(inp, wl, seconds: float):
     """The fp64 oracle on a bounded sample of the same workload (host cores)."""
-    from oracle.attention import Problem, attention_pairs_parallel
+    from oracle.attention import Problem, attention_pairs, attention_pairs_parallel
     from oracle.greedy import group_ids
     from query_union_paged_amd import synth
     workers = len(os.sched_getaffinity(0))
     pb = Problem(inp["q_bits"], inp["k_codes"], inp["v_codes"], inp["scales"], inp["sel_pages"])
-    # calibrate on a small stratified sample, then size the timed sample
     rng = np.random.default_rng(0)
+
     def sample(n):
         t = np.sort(rng.choice(wl.T, size=n, replace=False))
         return [(h, int(x)) for h in range(wl.H_kv) for x in t]
-    pairs = sample(16)
-    t0 = time.time()
-    attention_pairs_parallel(pb, pairs, workers=workers)
-    per_pair = (time.time() - t0) / len(pairs)
-    n = int(max(16, min(wl.T, seconds / max(per_pair, 1e-6) / wl.H_kv)))
-    pairs = sample(n)
-    t0 = time.time()
-    attention_pairs_parallel(pb, pairs, workers=workers)
-    dt = time.time() - t0
+    # calibrate in-process (no pool start-up in the estimate), then size the sample
+    from threadpoolctl import threadpool_limits
+    cal = sample(4)
+    with threadpool_limits(limits=1):
+        t0 = time.time()
+        attention_pairs(pb, cal)
+        per_pair = (time.time() - t0) / len(cal)
+    n = int(max(16, min(wl.T, seconds * workers / max(per_pair, 1e-6) / wl.H_kv)))
+    for _ in range(2):          # resize once if the pool ran far from the target time
+        pairs = sample(n)
+        t0 = time.time()
+        attention_pairs_parallel(pb, pairs, workers=workers)
+        dt = time.time() - t0
+        if dt >= 0.5 * seconds or n >= wl.T:
+            break
+        n = int(min(wl.T, n * seconds / max(dt, 1e-3)))
     sel = inp["sel_pages"]
     flops = 0.0
     for h, t in pairs:

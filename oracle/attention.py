@@ -46,7 +46,7 @@ class Problem:
         assert sel_pages.shape[:2] == (self.H_kv, self.T)
         self.S = sel_pages.shape[2]
         self.G = self.H_q // self.H_kv
-        self.q = decode_bf16(q_bits)                       # [T][H_q][D]
+        self.q_bits = q_bits                               # decoded row by row
         self.k_codes, self.v_codes = k_codes, v_codes
         self.scales = np.asarray(scales, dtype=np.float64)
         self.sel = np.asarray(sel_pages)
@@ -65,6 +65,15 @@ class Problem:
             v = decode_e4m3fn(self.v_codes[:, h]) * self.scales[1, :, h, None, None]
             self._vd[h] = np.ascontiguousarray(v.transpose(0, 2, 1))
         return self._vd[h]
+
+    @property
+    def q(self) -> np.ndarray:
+        """All of Q in fp64 [T][H_q][D] (small problems)."""
+        return decode_bf16(self.q_bits)
+
+    def q_rows(self, t: int, h: int) -> np.ndarray:
+        """Q[t][h*G:(h+1)*G] in fp64 [G][D]."""
+        return decode_bf16(self.q_bits[t, h * self.G:(h + 1) * self.G])
 
     def support(self, h: int, t: int) -> np.ndarray:
         row = self.sel[h, t]
@@ -87,7 +96,7 @@ def attention_query(pb: Problem, h: int, t: int) -> np.ndarray:
     keep = pos <= t
     kk = pb.k_hat(h)[sup].reshape(-1, pb.D)[keep]
     vv = pb.v_hat(h)[sup].reshape(-1, pb.D)[keep]
-    qq = pb.q[t, h * pb.G:(h + 1) * pb.G]
+    qq = pb.q_rows(t, h)
     s = (qq @ kk.T) / math.sqrt(pb.D)
     return _softmax_pv(s, vv)
 
@@ -123,7 +132,7 @@ def attention_groupwise(pb: Problem, ids: np.ndarray, g: int) -> np.ndarray:
             vv = pb.v_hat(h)[union].reshape(-1, pb.D)
             for t, sup in zip(members, sups):
                 mask = np.isin(page, list(sup)) & (pos <= t)
-                qq = pb.q[t, h * pb.G:(h + 1) * pb.G]
+                qq = pb.q_rows(t, h)
                 s = np.where(mask[None, :], (qq @ kk.T) / math.sqrt(pb.D), -np.inf)
                 if mask.any():
                     m = s.max(axis=1, keepdims=True)
@@ -142,7 +151,10 @@ _POOL_PB: Optional[Problem] = None
 
 
 def _work(chunk):
-    return attention_pairs(_POOL_PB, chunk)
+    # one BLAS thread per worker process: the pool already uses every core
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        return attention_pairs(_POOL_PB, chunk)
 
 
 def attention_pairs_parallel(pb: Problem, pairs: Sequence[tuple],

@@ -56,7 +56,7 @@ def dense_union(pb: Problem) -> np.ndarray:
                     keep = pos <= t
                     if not keep.any():
                         continue
-                    qq = pb.q[t, h * G:(h + 1) * G]
+                    qq = pb.q_rows(t, h)
                     s = (qq @ kk[keep].T) / math.sqrt(D)
                     m = s.max(axis=1)
                     e = np.exp(s - m[:, None])

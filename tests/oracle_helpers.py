@@ -10,7 +10,9 @@ def tiny_problem(T=64, Hq=4, Hkv=2, D=16, P=16, S=4, seed=0, sel=None, q_scale=1
     q = (torch.randn((T, Hq, D), generator=gen) * q_scale).to(torch.bfloat16)
     k = torch.randn((N, Hkv, P, D), generator=gen).to(torch.float8_e4m3fn)
     v = torch.randn((N, Hkv, P, D), generator=gen).to(torch.float8_e4m3fn)
-    scales = rng.uniform(0.05, 2.0, size=(2, N, Hkv)).astype(np.float32)
+    # dequantised values stay on the workloads' scale (|K|, |V| <~ 4.5): the bf16
+    # output's own rounding (2^-8 relative) then stays inside the 2e-2 bound
+    scales = rng.uniform(0.05, 1.0, size=(2, N, Hkv)).astype(np.float32)
     if sel is None:
         sel = np.full((Hkv, T, S), -1, dtype=np.int32)
         for h in range(Hkv):

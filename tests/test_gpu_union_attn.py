@@ -81,23 +81,6 @@ def test_8k_peaked_sampled():
     assert_close(gpu_rows(O, pairs, wl.G), oracle_rows(inp, pairs), "8k peaked")
 
 
-@pytest.mark.parametrize("name,arms", [("prefill_32k", ["regroup", "identity"]),
-                                       ("prefill_64k", ["regroup", "identity", "g1"]),
-                                       ("prefill_64k_70b", ["regroup", "identity"])])
-def test_large_sampled(name, arms):
-    wl = synth.WORKLOADS[name]
-    inp = host_inputs(name)
-    pairs = sample_pairs(wl)
-    ref = oracle_rows(inp, pairs)
-    for arm in arms:
-        log(f"[case] union {name} arm={arm}")
-        g = 1 if arm == "g1" else wl.g
-        O, _ = _run(inp, g, "identity" if arm == "identity" else "regroup", wl.W)
-        assert_close(gpu_rows(O, pairs, wl.G), ref, f"{name} {arm}")
-        del O
-        torch.cuda.empty_cache()
-
-
 @pytest.mark.parametrize("D,P,Hq,Hkv,S,g", [
     (64, 16, 4, 1, 8, 8), (64, 32, 8, 2, 5, 8), (128, 64, 8, 1, 4, 8),   # G = 8: two row tiles
     (128, 16, 2, 2, 6, 8), (64, 64, 16, 2, 3, 4), (128, 32, 4, 2, 7, 3),  # g = 3: ragged last group
@@ -131,6 +114,24 @@ def test_edge_cases_in_selection():
     assert_close(got, ref, "edge cases")
     o = O.float().cpu().numpy()
     assert np.all(o[100, 0:4] == 0) and np.all(o[7, 4:8] == 0)
+
+
+@pytest.mark.parametrize("name,arms", [("prefill_32k", ["regroup", "identity"]),
+                                       ("prefill_64k", ["regroup", "identity", "g1"]),
+                                       ("prefill_64k_70b", ["regroup", "identity"])])
+def test_large_sampled(name, arms):
+    wl = synth.WORKLOADS[name]
+    inp = host_inputs(name)
+    pairs = sample_pairs(wl)
+    ref = oracle_rows(inp, pairs)
+    log(f"[case] union {name}: {len(pairs)} sampled rows")
+    for arm in arms:
+        log(f"[case] union {name} arm={arm}")
+        g = 1 if arm == "g1" else wl.g
+        O, _ = _run(inp, g, "identity" if arm == "identity" else "regroup", wl.W)
+        assert_close(gpu_rows(O, pairs, wl.G), ref, f"{name} {arm}")
+        del O
+        torch.cuda.empty_cache()
 
 
 def test_invalid_arguments_raise():
