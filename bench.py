@@ -40,6 +40,11 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle sample time")
     ap.add_argument("--cold", type=int, default=5, help="cold-cache runs (MALL/L2 flushed)")
+    ap.add_argument("--gen-workers", type=int, default=16,
+                    help="processes for input generation (0: in-process, e.g. under a profiler)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="after the timed region, one plain 1 GiB device-to-device copy "
+                         "(reference dispatch for scaling HBM byte counters)")
     return ap.parse_args()
 
 
@@ -137,7 +142,8 @@ def main():
     wl = synth.WORKLOADS[args.workload]
     t0 = time.time()
     inp = synth.make_qkv(wl)
-    inp["sel_pages"] = synth.make_selection(wl, workers=min(16, len(os.sched_getaffinity(0))))
+    inp["sel_pages"] = synth.make_selection(
+        wl, workers=min(args.gen_workers, len(os.sched_getaffinity(0))))
     log(f"[bench] inputs {wl.name} generated in {time.time() - t0:.1f}s")
     dev = pw.to_device(inp)
     shp = pw.shape(*wl.shape_tuple())
@@ -174,6 +180,14 @@ def main():
     attn_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
     ms_per_step = wall * 1e3 / args.steps
     value = F_u / (ms_per_step * 1e-3) / 1e12
+
+    if args.copy_calib:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)                       # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
 
     # cold runs: a 1 GiB write between runs evicts MALL and L2
     cold = []

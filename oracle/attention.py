@@ -174,8 +174,12 @@ def attention_pairs_parallel(pb: Problem, pairs: Sequence[tuple],
     chunks = [c for c in chunks if c]
     _POOL_PB = pb
     try:
-        with mp.get_context("fork").Pool(workers) as pool:
+        pool = mp.get_context("fork").Pool(workers)
+        try:
             parts = pool.map(_work, chunks)
+        finally:                     # let workers exit on their own (no SIGTERM)
+            pool.close()
+            pool.join()
     finally:
         _POOL_PB = None
     out = np.empty((len(pairs), pb.G, pb.D))

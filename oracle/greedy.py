@@ -98,8 +98,12 @@ def group_ids(sel: np.ndarray, N: int, W: int, g: int,
     workers = workers if workers is not None else 1
     if workers > 1 and len(jobs) > 1:
         import multiprocessing as mp
-        with mp.get_context("fork").Pool(workers) as pool:
+        pool = mp.get_context("fork").Pool(workers)
+        try:
             results = pool.map(_group_windows, [j for _, j in jobs])
+        finally:                     # let workers exit on their own (no SIGTERM)
+            pool.close()
+            pool.join()
     else:
         results = [_group_windows(j) for _, j in jobs]
     for (h, _), res in zip(jobs, results):

@@ -6,10 +6,10 @@
 // query IDs without materialising a reordered Q tensor or cross-page partial
 // outputs.
 //
-// Mapping on CDNA4.  One wave owns one group (g query IDs of one KV head,
-// M = g*G query rows <= 64 = NT tiles of 32) and walks the group's union of
-// pages in ascending page order; four waves (four groups) share a workgroup
-// only for scheduling.  Per page (64 keys):
+// Mapping on CDNA4.  One wave owns one 32-row tile of one group (g query IDs
+// of one KV head, M = g*G query rows <= 64, so one or two waves per group) and
+// walks the group's union of pages in ascending page order; four waves share a
+// workgroup only for scheduling.  Per page (64 keys):
 //   S^T = K_page * Q^T     v_mfma_f32_32x32x16_bf16, keys are the MFMA rows
 //                          and query rows the columns, so each lane holds one
 //                          query row (lane & 31) and 32 of its 64 keys;
@@ -45,6 +45,8 @@ struct UAParams {
   uint16_t* O;
   int T, Hq, Hkv, G, P, N, S, g;
   int groups_per_head, total_groups;
+  int n_rt;          // 32-row tiles per group (ceil(g * G / 32)): one wave each
+  int total_items;   // total_groups * n_rt
   int n_umax;        // list capacity per wave (>= any union size)
   int lds_wave;      // bytes of LDS per wave
   float qk_scale;    // log2(e) / sqrt(D)
@@ -57,13 +59,26 @@ __device__ __forceinline__ int tile_key(int i, int kt) {
   return 32 * ((i >> 2) & 1) + 16 * kt + 4 * (i >> 3) + (i & 3);
 }
 
+// Lanes l and l ^ 32 hold the two key halves of the same query row: combine
+// them with one VALU lane swap (no LDS round trip).
+__device__ __forceinline__ float half_max(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+}
+
 __device__ __forceinline__ uint4 load16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-template <int D, int NT>
-__global__ __launch_bounds__(256) void union_attn_kernel(UAParams p) {
-  constexpr int KS = D / 16;     // MFMA k-steps over d (QK^T)
+template <int D, bool P64, bool PIPE>
+__global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams p) {
+  constexpr int NT = 1;          // one 32-row tile per wave
+  // P64: pages of exactly 64 keys (no key-range guards); otherwise P in {16, 32}.
+  const int P = P64 ? 64 : p.P;
   constexpr int KCH = D / 32;    // uint4 chunks of K per lane per key tile
   constexpr int DT = D / 32;     // output tiles over d (PV)
   extern __shared__ __align__(16) unsigned char smem[];
@@ -79,8 +94,10 @@ __global__ __launch_bounds__(256) void union_attn_kernel(UAParams p) {
   const int nb = gridDim.x, b = blockIdx.x;
   const int xcd = b & 7, per = nb >> 3, extra = nb & 7;
   const int lb = xcd * per + min(xcd, extra) + (b >> 3);
-  const int gid = lb * 4 + wave;
-  if (gid >= p.total_groups) return;
+  const int wid = lb * 4 + wave;
+  if (wid >= p.total_items) return;
+  const int gid = wid / p.n_rt;
+  const int rt = wid - gid * p.n_rt;        // which 32-row tile of the group
   const int h = gid / p.groups_per_head;
   const int g0 = (gid - h * p.groups_per_head) * p.g;
   const int gm = min(p.g, p.T - g0);
@@ -133,12 +150,17 @@ __global__ __launch_bounds__(256) void union_attn_kernel(UAParams p) {
   }
   wave_sync();
 
-  // ---- per-lane query rows and Q operands (B of S^T = K Q^T)
+  // ---- per-lane query rows and Q operands (B of S^T = K Q^T).  Each bf16 row
+  // is scaled by a power of two (absmax into [128, 256)) and split exactly into
+  // two e4m3fn parts, hi + lo, so that K^T can run on the FP8 MFMA straight
+  // from the cache bytes; 2^-e is folded back into the score scale.
+  constexpr int KQ = D / 64;     // fp8 MFMA k-steps (64 d each, 32 per lane half)
   int slot[NT], trow[NT], qhead[NT];
-  bf16x8 qB[NT][KS];
+  float rscale[NT];
+  i32x8 qhi[NT][KQ], qlo[NT][KQ];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const int n = 32 * nt + col;
+    const int n = 32 * (rt + nt) + col;
     const int s = n / p.G;
     const int t = __shfl(my_t, s & 63);
     const bool ok = (s < gm) && (t >= 0);
@@ -146,10 +168,44 @@ __global__ __launch_bounds__(256) void union_attn_kernel(UAParams p) {
     trow[nt] = ok ? t : -1;
     qhead[nt] = h * p.G + (n - s * p.G);
     const uint16_t* qp = p.Q + ((size_t)(ok ? t : 0) * p.Hq + qhead[nt]) * D + (D / 2) * hf;
+    float q[D / 2];
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      const uint4 v = ok ? *reinterpret_cast<const uint4*>(qp + 8 * ks) : make_uint4(0, 0, 0, 0);
-      qB[nt][ks] = as_bf16x8(v);
+    for (int c = 0; c < D / 16; ++c) {
+      const uint4 v = ok ? *reinterpret_cast<const uint4*>(qp + 8 * c) : make_uint4(0, 0, 0, 0);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        q[8 * c + 2 * k] = __uint_as_float(w[k] << 16);
+        q[8 * c + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      }
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < D / 2; ++i) amax = fmaxf(amax, fabsf(q[i]));
+    amax = fmaxf(amax, __shfl_xor(amax, 32));
+    int e = 0;
+    if (amax > 0.f) {
+      int ex;
+      frexpf(amax, &ex);
+      e = 8 - ex;                  // amax * 2^e in [128, 256)
+    }
+    rscale[nt] = ldexpf(1.f, -e);
+#pragma unroll
+    for (int ks = 0; ks < KQ; ++ks) {
+#pragma unroll
+      for (int w = 0; w < 8; ++w) {
+        const float* x = q + 32 * ks + 4 * w;
+        const float x0 = ldexpf(x[0], e), x1 = ldexpf(x[1], e);
+        const float x2 = ldexpf(x[2], e), x3 = ldexpf(x[3], e);
+        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+        hi = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hi, true);
+        const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
+        const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01[0], x1 - h01[1], 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23[0], x3 - h23[1], lo, true);
+        qhi[nt][ks][w] = hi;
+        qlo[nt][ks][w] = lo;
+      }
     }
   }
 
@@ -165,81 +221,81 @@ __global__ __launch_bounds__(256) void union_attn_kernel(UAParams p) {
       for (int r = 0; r < 16; ++r) acc[nt][dt][r] = 0.f;
   }
 
-  const size_t page_stride = (size_t)p.Hkv * p.P * D;   // bytes between pages
-  const uint8_t* kbase = p.K + (size_t)h * p.P * D;
-  const uint8_t* vbase = p.V + (size_t)h * D * p.P;
+  const size_t page_stride = (size_t)p.Hkv * P * D;     // bytes between pages
+  const uint8_t* kbase = p.K + (size_t)h * P * D;
+  const uint8_t* vbase = p.V + (size_t)h * D * P;
   int krow[2];
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) krow[kt] = tile_key(col, kt);
-  const int vbytes = min(max(p.P - 32 * hf, 0), 32);   // valid V bytes of this lane's row
+  const int vbytes = min(max(P - 32 * hf, 0), 32);     // valid V bytes of this lane's row
 
-  uint4 kraw[2][KCH], vraw[DT][2];
-  auto load_k = [&](int u) {
+  // Two pages in flight.  Step `up` (buffer c = up & 1, n = c ^ 1):
+  //   prefetch K(up+2) into kbuf[c]      (K(up) was consumed by QK(up))
+  //   QK(up+1) on kbuf[n] -> sacc[n]     (matrix cores ...
+  //   softmax(up) on sacc[c]             ... while the VALU works on page up)
+  //   PV(up) with vbuf[c] -> acc
+  //   prefetch V(up+2) into vbuf[c]
+  // Loads past the last page re-read the last page (one redundant page per
+  // group keeps the prefetch unconditional).
+  uint4 kbuf[2][2][KCH], vbuf[2][DT][2];
+  f32x16 sacc[2][NT][2];
+  float ksr[2], vsr[2];
+  auto page_of = [&](int i) { return (int)(list[min(i, n_u - 1)] & 0xFFFF); };
+  auto load_k = [&](uint4 (&kr)[2][KCH], int u) {
     const uint8_t* kp = kbase + (size_t)u * page_stride + (D / 2) * hf;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int c = 0; c < KCH; ++c)
-        kraw[kt][c] = (krow[kt] < p.P) ? load16(kp + (size_t)krow[kt] * D + 16 * c)
-                                       : make_uint4(0, 0, 0, 0);
+        kr[kt][c] = (P64 || krow[kt] < P) ? load16(kp + (size_t)krow[kt] * D + 16 * c)
+                                          : make_uint4(0, 0, 0, 0);
   };
-  auto load_v = [&](int u) {
+  auto load_v = [&](uint4 (&vr)[DT][2], int u) {
     const uint8_t* vp = vbase + (size_t)u * page_stride + 32 * hf;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
-      const uint8_t* row = vp + (size_t)(32 * dt + col) * p.P;
-      vraw[dt][0] = (vbytes >= 16) ? load16(row) : make_uint4(0, 0, 0, 0);
-      vraw[dt][1] = (vbytes >= 32) ? load16(row + 16) : make_uint4(0, 0, 0, 0);
+      const uint8_t* row = vp + (size_t)(32 * dt + col) * P;
+      vr[dt][0] = (P64 || vbytes >= 16) ? load16(row) : make_uint4(0, 0, 0, 0);
+      vr[dt][1] = (P64 || vbytes >= 32) ? load16(row + 16) : make_uint4(0, 0, 0, 0);
     }
   };
-
   const float* kscale = p.scales + h;                       // [N][Hkv]
   const float* vscale = p.scales + (size_t)p.N * p.Hkv + h;
-  float ks_raw = 1.f, vs_raw = 1.f;
-  if (n_u > 0) {
-    const int u0 = list[0] & 0xFFFF;
-    load_k(u0);
-    load_v(u0);
-    ks_raw = kscale[(size_t)u0 * p.Hkv];
-    vs_raw = vscale[(size_t)u0 * p.Hkv];
-  }
-
-  for (int up = 0; up < n_u; ++up) {
-    const uint32_t ent = list[up];
-    const int u = ent & 0xFFFF;
-    const uint32_t mbits = ent >> 16;
-    const float ksc = ks_raw * p.qk_scale;
-    const float lvs = __builtin_amdgcn_logf(vs_raw);    // log2
-    const float ivs = __builtin_amdgcn_rcpf(vs_raw);
-    const int u_next = (up + 1 < n_u) ? (int)(list[up + 1] & 0xFFFF) : -1;
-    if (u_next >= 0) {
-      ks_raw = kscale[(size_t)u_next * p.Hkv];
-      vs_raw = vscale[(size_t)u_next * p.Hkv];
-    }
-
-    // S^T = K Q^T
-    f32x16 sacc[NT][2];
+  // S^T = K (Qhi + Qlo)^T on the FP8 MFMA
+  auto qk = [&](const uint4 (&kr)[2][KCH], f32x16 (&sc)[NT][2]) {
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[nt][kt][r] = 0.f;
+        for (int r = 0; r < 16; ++r) sc[nt][kt][r] = 0.f;
+    // key tiles innermost: consecutive MFMAs accumulate into different tiles
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+    for (int ks = 0; ks < KQ; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 w = kraw[kt][ks >> 1];
-        const bf16x8 a = (ks & 1) ? fp8x8_to_bf16(w.z, w.w) : fp8x8_to_bf16(w.x, w.y);
+      for (int part = 0; part < 2; ++part) {
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          sacc[nt][kt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qB[nt][ks], sacc[nt][kt], 0, 0, 0);
+        for (int kt = 0; kt < 2; ++kt) {
+          const uint4 w0 = kr[kt][2 * ks], w1 = kr[kt][2 * ks + 1];
+          const i32x8 a = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w,
+                           (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt)
+            sc[nt][kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                a, part ? qlo[nt][ks] : qhi[nt][ks], sc[nt][kt], 0, 0, 0, 127, 0, 127);
+        }
       }
     }
-    if (u_next >= 0) load_k(u_next);
-
+  };
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  // mask, online softmax (log2 domain, v_scale folded into the exponent), PV
+  auto softmax_pv = [&](f32x16 (&sc)[NT][2], const uint4 (&vr)[DT][2], int u, uint32_t mbits,
+                        float ks_raw, float vs_raw) {
+    const float ksc0 = ks_raw * p.qk_scale;
+    const float lvs = __builtin_amdgcn_logf(vs_raw);    // log2
+    const float ivs = __builtin_amdgcn_rcpf(vs_raw);
     // causal / page-size mask, only where some key can lie after a member
-    const bool need_mask = (p.P < 64) || (u * p.P + p.P - 1 > tmin);
+    const bool need_mask = !P64 || (u * P + P - 1 > tmin);
     if (need_mask) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -248,11 +304,9 @@ __global__ __launch_bounds__(256) void union_attn_kernel(UAParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = 32 * hf + 16 * kt + r;
-            if (key >= p.P || u * p.P + key > trow[nt]) sacc[nt][kt][r] = -INFINITY;
+            if ((!P64 && key >= P) || u * P + key > trow[nt]) sc[nt][kt][r] = -INFINITY;
           }
     }
-
-    // online softmax (log2 domain, v_scale folded into the exponent)
     bf16x8 pB[NT][4];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -260,9 +314,10 @@ __global__ __launch_bounds__(256) void union_attn_kernel(UAParams p) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[nt][kt][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[nt][kt][r], sc[nt][kt][r + 1]));
+      mx = half_max(mx);
       const bool member = slot[nt] >= 0 && ((mbits >> slot[nt]) & 1u);
+      const float ksc = ksc0 * rscale[nt];
       const float mx2 = mx * ksc;
       const float m_new = (member && mx2 > m_run[nt] + kTau) ? mx2 : m_run[nt];
       const float alpha = (m_new == m_run[nt]) ? 1.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
@@ -270,13 +325,21 @@ __global__ __launch_bounds__(256) void union_attn_kernel(UAParams p) {
       const float bias = (member && m_new > -INFINITY) ? (lvs - m_new) : -INFINITY;
       float ps = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
+      for (int q = 0; q < 4; ++q) {
+        bf16x8 v;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(sacc[nt][kt][r], ksc, bias));
-          sacc[nt][kt][r] = e;
-          ps += e;
+        for (int e = 0; e < 8; e += 2) {
+          const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[nt][q >> 1][8 * (q & 1) + e], ksc, bias));
+          const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[nt][q >> 1][8 * (q & 1) + e + 1], ksc, bias));
+          bf16x2 pr;
+          pr[0] = (__bf16)e0;
+          pr[1] = (__bf16)e1;
+          ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
+          v[e] = pr[0];
+          v[e + 1] = pr[1];
         }
+        pB[nt][q] = v;
+      }
       l_run[nt] = l_run[nt] * alpha + ps * ivs;
       if (__ballot(alpha != 1.f)) {
 #pragma unroll
@@ -284,34 +347,83 @@ __global__ __launch_bounds__(256) void union_attn_kernel(UAParams p) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[nt][dt][r] *= alpha;
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bf16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = (__bf16)sacc[nt][q >> 1][8 * (q & 1) + e];
-        pB[nt][q] = v;
-      }
     }
-
-    // O^T += V^T P^T
+    // O^T += V^T P^T  (d tiles innermost: consecutive MFMAs are independent)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
+    for (int q = 0; q < 4; ++q) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 w = vraw[dt][q >> 1];
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint4 w = vr[dt][q >> 1];
         const bf16x8 a = (q & 1) ? fp8x8_to_bf16(w.z, w.w) : fp8x8_to_bf16(w.x, w.y);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
           acc[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pB[nt][q], acc[nt][dt], 0, 0, 0);
       }
     }
-    if (u_next >= 0) load_v(u_next);
+  };
+
+  if (PIPE) {
+    // QK(up+1) on the matrix cores overlaps softmax(up) on the VALU; K and V
+    // are fetched two pages ahead (one wave per SIMD, 512 registers).
+    if (n_u > 0) {
+      const int u0 = page_of(0), u1 = page_of(1);
+      load_k(kbuf[0], u0);
+      load_v(vbuf[0], u0);
+      load_k(kbuf[1], u1);
+      load_v(vbuf[1], u1);
+      ksr[0] = kscale[(size_t)u0 * p.Hkv];
+      vsr[0] = vscale[(size_t)u0 * p.Hkv];
+      ksr[1] = kscale[(size_t)u1 * p.Hkv];
+      vsr[1] = vscale[(size_t)u1 * p.Hkv];
+      qk(kbuf[0], sacc[0]);
+    }
+    for (int up0 = 0; up0 < n_u; up0 += 2) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const int up = up0 + c;
+        if (up < n_u) {
+          const int n = c ^ 1;
+          const uint32_t ent = list[up];
+          const float ks_c = ksr[c], vs_c = vsr[c];
+          const int u2 = page_of(up + 2);
+          load_k(kbuf[c], u2);
+          ksr[c] = kscale[(size_t)u2 * p.Hkv];
+          vsr[c] = vscale[(size_t)u2 * p.Hkv];
+          if (up + 1 < n_u) qk(kbuf[n], sacc[n]);
+          softmax_pv(sacc[c], vbuf[c], ent & 0xFFFF, ent >> 16, ks_c, vs_c);
+          load_v(vbuf[c], u2);
+        }
+      }
+    }
+  } else {
+    // Plain order with one page of K/V ahead, two waves per SIMD overlapping
+    // each other's matrix and vector work.
+    if (n_u > 0) {
+      const int u0 = page_of(0);
+      load_k(kbuf[0], u0);
+      load_v(vbuf[0], u0);
+      ksr[0] = kscale[(size_t)u0 * p.Hkv];
+      vsr[0] = vscale[(size_t)u0 * p.Hkv];
+    }
+    for (int up = 0; up < n_u; ++up) {
+      const uint32_t ent = list[up];
+      const float ks_c = ksr[0], vs_c = vsr[0];
+      const int u1 = page_of(up + 1);
+      qk(kbuf[0], sacc[0]);
+      __builtin_amdgcn_sched_barrier(0);    // K registers are free after the MFMAs read them
+      load_k(kbuf[0], u1);
+      ksr[0] = kscale[(size_t)u1 * p.Hkv];
+      vsr[0] = vscale[(size_t)u1 * p.Hkv];
+      softmax_pv(sacc[0], vbuf[0], ent & 0xFFFF, ent >> 16, ks_c, vs_c);
+      __builtin_amdgcn_sched_barrier(0);
+      load_v(vbuf[0], u1);
+    }
   }
 
   // ---- epilogue: normalise and write each owned row once
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
-    const float l_tot = l_run[nt] + __shfl_xor(l_run[nt], 32);
+    const float l_tot = half_sum(l_run[nt]);
     const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
     if (trow[nt] < 0) continue;
     uint16_t* op = p.O + ((size_t)trow[nt] * p.Hq + qhead[nt]) * D;
@@ -330,9 +442,17 @@ __global__ __launch_bounds__(256) void union_attn_kernel(UAParams p) {
   }
 }
 
-template <int D, int NT>
-hipError_t launch_dn(const UAParams& prm, int blocks, size_t lds, hipStream_t stream) {
-  hipLaunchKernelGGL((union_attn_kernel<D, NT>), dim3(blocks), dim3(256), lds, stream, prm);
+#ifndef PW_UA_PIPE
+#define PW_UA_PIPE 0   // 1: software-pipelined schedule at one wave per SIMD
+#endif
+
+template <int D>
+hipError_t launch_d(const UAParams& prm, int blocks, size_t lds, hipStream_t stream) {
+  constexpr bool pipe = PW_UA_PIPE != 0;
+  if (prm.P == 64)
+    hipLaunchKernelGGL((union_attn_kernel<D, true, pipe>), dim3(blocks), dim3(256), lds, stream, prm);
+  else
+    hipLaunchKernelGGL((union_attn_kernel<D, false, pipe>), dim3(blocks), dim3(256), lds, stream, prm);
   return hipGetLastError();
 }
 
@@ -351,13 +471,12 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
   const int mask_bytes = ((s.N_pages + 3) / 4) * 4;
   prm.lds_wave = ((prm.n_umax * 4 + mask_bytes) + 15) / 16 * 16;
   prm.qk_scale = kLog2e / sqrtf((float)s.D);
-  const int blocks = (prm.total_groups + 3) / 4;
+  prm.n_rt = (g * prm.G + 31) / 32;
+  prm.total_items = prm.total_groups * prm.n_rt;
+  const int blocks = (prm.total_items + 3) / 4;
   const size_t lds = (size_t)prm.lds_wave * 4;
-  const int nt = (g * prm.G + 31) / 32;
-  if (s.D == 128) return nt == 1 ? launch_dn<128, 1>(prm, blocks, lds, stream)
-                                 : launch_dn<128, 2>(prm, blocks, lds, stream);
-  return nt == 1 ? launch_dn<64, 1>(prm, blocks, lds, stream)
-                 : launch_dn<64, 2>(prm, blocks, lds, stream);
+  return s.D == 128 ? launch_d<128>(prm, blocks, lds, stream)
+                    : launch_d<64>(prm, blocks, lds, stream);
 }
 
 }  // namespace pw

@@ -16,7 +16,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpageweaver.so")
+# PAGEWEAVER_LIB may name another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("PAGEWEAVER_LIB") or os.path.join(_HERE, "libpageweaver.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "pageweaver.h")
 
 if not os.path.exists(LIB_PATH):

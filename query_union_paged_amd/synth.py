@@ -192,8 +192,12 @@ def make_selection(wl: Workload, variant: int = 0, workers: int = 0) -> np.ndarr
     jobs = [(wl, wl.seed_for(variant), h) for h in range(wl.H_kv)]
     if workers > 1 and wl.H_kv > 1:
         import multiprocessing as mp
-        with mp.get_context("fork").Pool(min(workers, wl.H_kv)) as pool:
+        pool = mp.get_context("fork").Pool(min(workers, wl.H_kv))
+        try:
             heads = pool.map(_select_head_seeded, jobs)
+        finally:                     # let workers exit on their own (no SIGTERM)
+            pool.close()
+            pool.join()
     else:
         heads = [_select_head_seeded(j) for j in jobs]
     return np.stack(heads, axis=0)
