@@ -245,6 +245,21 @@ def main():
             arms[name] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12,
                           "union_pages_mean": float(us.mean()), "union_pages_total": int(us.sum())}
         arms["regroup_gain_vs_identity"] = arms["identity_union8"]["ms"] / ms_per_step
+        # the direct KV-page union (design-study comparison)
+        ws = torch.empty(pw.pw_dense_union_ref_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
+        pw.pw_dense_union_ref(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
+                              dev["sel_pages"], O=O, workspace=ws)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(2):
+            pw.pw_dense_union_ref(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
+                                  dev["sel_pages"], O=O, workspace=ws)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / 2
+        arms["direct_page_union"] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12,
+                                     "workspace_GiB": ws.numel() / 2 ** 30}
+        del ws
 
     cpu = None
     if not args.no_cpu:

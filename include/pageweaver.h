@@ -163,8 +163,9 @@ pw_status pw_union_attention(const pw_shape* shape, const uint16_t* Q,
  * each query's partials by log-sum-exp into O.  Same O as
  * pw_union_attention up to floating-point order.
  *
- * In/Out/support: as pw_union_attention (no query_ids); queries are processed
- * in chunks sized so that the workspace stays bounded.
+ * In/Out/support: as pw_union_attention (no query_ids), plus G <= 8 and
+ * N_pages <= 4096; queries are processed in chunks sized so that the
+ * workspace stays within about 4 GiB.
  * Workspace: pw_dense_union_ref_workspace_bytes(shape) bytes, 256-byte
  * aligned.
  * ------------------------------------------------------------------------- */

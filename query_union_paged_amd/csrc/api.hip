@@ -124,6 +124,10 @@ pw_status pw_dense_union_ref(const pw_shape* shape, const uint16_t* Q, const uin
     return fail(PW_ERR_NULL, "Q, K_fp8, V_fp8, scales, sel_pages and O are required");
   st = check_attention_support(shape, 1);
   if (st != PW_OK) return st;
+  if (shape->H_q / shape->H_kv > 8)
+    return fail(PW_ERR_UNSUPPORTED, "G = %d exceeds 8 for the page-pair tiles", shape->H_q / shape->H_kv);
+  if (shape->N_pages > 4096)
+    return fail(PW_ERR_UNSUPPORTED, "N_pages = %d exceeds 4096 for the page-pair lists", shape->N_pages);
   const size_t need = pw::dense_union_workspace(*shape);
   if (need > 0 && !ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
   if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);

@@ -1,15 +1,172 @@
-// Direct KV-page union (design-study comparison).  Work in progress: the
-// launcher reports hipErrorNotSupported until the pair kernels land.
+// Direct KV-page union: the pages' design-study alternative to query unions.
+//
+// "PageWeaver: KV-Guided Query Unions for Sparse Attention", Abstract: a
+// direct KV-page union implementation studies non-local reuse against the
+// cost of reducing partial outputs.  AI Radio episode on the paper, "Paper
+// summary": it works on disjoint page pairs and uses the full membership of
+// each page to form common or exclusive query lists.
+//
+// Per chunk of Tc queries (all KV heads), on the caller's stream:
+//   1. zero the per-pair list lengths;
+//   2. pair_entries_kernel: one thread per (KV head, query) sets its page
+//      bitset in LDS, walks its pairs (2k, 2k+1) in ascending order and appends
+//      (query, partial slot, which pages) to pair k's list -- the pair's full
+//      membership; an entry with both pages is on the common list, one page
+//      on an exclusive list;
+//   3. pair attention (union_attn.hip, pair mode): tiles of 8 entries of a
+//      list compute (m, l, acc) over their own visible keys of the pair;
+//   4. merge_kernel: one wave per (KV head, query) combines its partials by
+//      log-sum-exp into O.
+// The list order within a pair depends on atomics, but every partial has a
+// fixed slot and a row's arithmetic does not depend on the other rows of its
+// tile, so the result is deterministic.
 #include "pw_internal.h"
 
 namespace pw {
+namespace {
 
-size_t dense_union_workspace(const pw_shape&) { return 0; }
+constexpr size_t kBudget = size_t(4) << 30;   // workspace bound (bytes)
 
-hipError_t launch_dense_union(const pw_shape&, const uint16_t*, const uint8_t*, const uint8_t*,
-                              const float*, const int32_t*, uint16_t*, void*, size_t,
-                              hipStream_t) {
-  return hipErrorNotSupported;
+struct DUPlan {
+  int Np, maxp, Tc, NW;
+  size_t off_count, off_npairs, off_list, off_part, total;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+DUPlan plan(const pw_shape& s) {
+  DUPlan d;
+  const int G = s.H_q / s.H_kv;
+  d.Np = (s.N_pages + 1) / 2;
+  d.maxp = s.S < d.Np ? s.S : d.Np;
+  d.NW = (s.N_pages + 31) / 32;
+  const size_t per_token = (size_t)s.H_kv * ((size_t)d.maxp * G * (s.D + 4) * 4 + (size_t)d.Np * 8 + 4);
+  size_t tc = kBudget / per_token;
+  tc = tc / 64 * 64;
+  if (tc < 64) tc = 64;
+  const size_t tmax = ((size_t)s.T + 63) / 64 * 64;
+  if (tc > tmax) tc = tmax;
+  d.Tc = (int)tc;
+  d.off_count = 0;
+  d.off_npairs = align256((size_t)s.H_kv * d.Np * 4);
+  d.off_list = d.off_npairs + align256((size_t)s.H_kv * d.Tc * 4);
+  d.off_part = d.off_list + align256((size_t)s.H_kv * d.Np * d.Tc * 8);
+  d.total = d.off_part + align256((size_t)s.H_kv * d.Tc * d.maxp * G * (s.D + 4) * 4);
+  return d;
+}
+
+__global__ void zero_kernel(int* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+}
+
+__global__ __launch_bounds__(64) void pair_entries_kernel(const int32_t* __restrict__ sel, int T,
+                                                         int S, int N, int NW, int Np, int Tc,
+                                                         int maxp, int t0, int* pcount,
+                                                         int* npairs, int2* plist) {
+  extern __shared__ uint32_t words[];              // [64][NW + 1]
+  const int h = blockIdx.y;
+  const int tl = blockIdx.x * 64 + threadIdx.x;    // query within the chunk
+  const int t = t0 + tl;
+  uint32_t* w = words + threadIdx.x * (NW + 1);
+  for (int i = 0; i < NW; ++i) w[i] = 0;
+  if (tl >= Tc || t >= T) return;
+  const int32_t* row = sel + ((size_t)h * T + t) * S;
+  for (int s = 0; s < S; ++s) {
+    const int u = row[s];
+    if (u >= 0 && u < N) w[u >> 5] |= 1u << (u & 31);
+  }
+  int j = 0;
+  for (int i = 0; i < NW; ++i) {
+    const uint32_t x = w[i];
+    uint32_t pm = (x | (x >> 1)) & 0x55555555u;    // pairs with at least one page
+    while (pm) {
+      const int bit = __builtin_ctz(pm);
+      pm &= pm - 1;
+      const int k = i * 16 + (bit >> 1);
+      const int kind = (x >> bit) & 3;             // 1: page 2k, 2: page 2k+1, 3: both
+      const int slot = (h * Tc + tl) * maxp + j++;
+      const int pos = atomicAdd(&pcount[h * Np + k], 1);
+      plist[((size_t)h * Np + k) * Tc + pos] = make_int2(tl, slot | (kind << 30));
+    }
+  }
+  npairs[h * Tc + tl] = j;
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ partials,
+                                                   const int* __restrict__ npairs,
+                                                   uint16_t* __restrict__ O, int T, int Hq,
+                                                   int G, int Tc, int maxp, int t0) {
+  constexpr int PER = D / 64;                      // d values per lane
+  const int h = blockIdx.y;
+  const int tl = blockIdx.x;
+  const int t = t0 + tl;
+  if (t >= T) return;
+  const int lane = threadIdx.x;
+  const int n = npairs[h * Tc + tl];
+  const size_t slot0 = ((size_t)h * Tc + tl) * maxp;
+  for (int j = 0; j < G; ++j) {
+    float M = -INFINITY, L = 0.f, A[PER];
+#pragma unroll
+    for (int q = 0; q < PER; ++q) A[q] = 0.f;
+    for (int jj = 0; jj < n; ++jj) {
+      const float* pp = partials + ((slot0 + jj) * G + j) * (D + 4);
+      const float m = pp[0], l = pp[1];
+      if (!(l > 0.f)) continue;                    // no visible key in this pair
+      const float Mn = fmaxf(M, m);
+      const float a = exp2f(M - Mn), c = exp2f(m - Mn);
+      L = L * a + l * c;
+#pragma unroll
+      for (int q = 0; q < PER; ++q) A[q] = A[q] * a + pp[4 + lane + 64 * q] * c;
+      M = Mn;
+    }
+    const float inv = (L > 0.f) ? 1.f / L : 0.f;
+    uint16_t* op = O + ((size_t)t * Hq + h * G + j) * D;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+      const __bf16 v = (__bf16)(A[q] * inv);
+      op[lane + 64 * q] = __builtin_bit_cast(uint16_t, v);
+    }
+  }
+}
+
+}  // namespace
+
+size_t dense_union_workspace(const pw_shape& s) { return plan(s).total; }
+
+hipError_t launch_dense_union(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
+                              const uint8_t* V, const float* scales, const int32_t* sel,
+                              uint16_t* O, void* ws, size_t ws_bytes, hipStream_t stream) {
+  const DUPlan d = plan(s);
+  if (ws_bytes < d.total) return hipErrorInvalidValue;
+  char* base = static_cast<char*>(ws);
+  int* pcount = reinterpret_cast<int*>(base + d.off_count);
+  int* npairs = reinterpret_cast<int*>(base + d.off_npairs);
+  int2* plist = reinterpret_cast<int2*>(base + d.off_list);
+  float* partials = reinterpret_cast<float*>(base + d.off_part);
+  const int G = s.H_q / s.H_kv;
+  for (int t0 = 0; t0 < s.T; t0 += d.Tc) {
+    const int n_count = s.H_kv * d.Np;
+    hipLaunchKernelGGL(zero_kernel, dim3((n_count + 255) / 256), dim3(256), 0, stream, pcount,
+                       n_count);
+    const int tcur = (s.T - t0 < d.Tc) ? s.T - t0 : d.Tc;
+    hipLaunchKernelGGL(pair_entries_kernel, dim3((tcur + 63) / 64, s.H_kv), dim3(64),
+                       (size_t)64 * (d.NW + 1) * 4, stream, sel, s.T, s.S, s.N_pages, d.NW, d.Np,
+                       d.Tc, d.maxp, t0, pcount, npairs, plist);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = launch_pair_attention(s, Q, K, V, scales, plist, pcount, partials, d.Np, d.Tc, t0, stream);
+    if (e != hipSuccess) return e;
+    if (s.D == 128)
+      hipLaunchKernelGGL(merge_kernel<128>, dim3(tcur, s.H_kv), dim3(64), 0, stream, partials,
+                         npairs, O, s.T, s.H_q, G, d.Tc, d.maxp, t0);
+    else
+      hipLaunchKernelGGL(merge_kernel<64>, dim3(tcur, s.H_kv), dim3(64), 0, stream, partials,
+                         npairs, O, s.T, s.H_q, G, d.Tc, d.maxp, t0);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace pw

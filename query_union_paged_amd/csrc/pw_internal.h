@@ -55,6 +55,10 @@ hipError_t launch_group(const pw_shape& s, const int32_t* sel, int W, int g, int
 hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
                                   const uint8_t* V, const float* scales, const int32_t* sel,
                                   const int32_t* ids, int g, uint16_t* O, hipStream_t stream);
+hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
+                                 const uint8_t* V, const float* scales, const int2* plist,
+                                 const int* pcount, float* partials, int Np, int Tc, int t0,
+                                 hipStream_t stream);
 size_t dense_union_workspace(const pw_shape& s);
 hipError_t launch_dense_union(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
                               const uint8_t* V, const float* scales, const int32_t* sel,

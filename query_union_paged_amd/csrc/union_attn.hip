@@ -50,7 +50,14 @@ struct UAParams {
   int n_umax;        // list capacity per wave (>= any union size)
   int lds_wave;      // bytes of LDS per wave
   float qk_scale;    // log2(e) / sqrt(D)
+  // page-pair mode (direct KV-page union): per (KV head, pair) entry lists
+  const int2* plist;   // [H_kv][Np][Tc] (token - t0, partial slot | pages << 30)
+  const int* pcount;   // [H_kv][Np] entries per list
+  float* partials;     // [slot][G][D + 4]: m, l, -, -, acc[D]
+  int Np, Tc, t0, tiles_per_pair;
 };
+
+enum : int { kUnionMode = 0, kPairMode = 1 };
 
 // Physical key held by MFMA row i of key tile kt.  Output register r of a lane
 // in half `hf` holds MFMA row 8*(r/4) + 4*hf + r%4; with this map it holds
@@ -74,7 +81,10 @@ __device__ __forceinline__ uint4 load16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
-template <int D, bool P64, bool PIPE>
+// MODE kUnionMode: groups of query IDs, union of their selected pages, O out.
+// MODE kPairMode: up to 8 entries of one page pair's membership list, the pair's
+// pages they selected, unnormalised partials out (direct KV-page union).
+template <int D, bool P64, bool PIPE, int MODE>
 __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams p) {
   constexpr int NT = 1;          // one 32-row tile per wave
   // P64: pages of exactly 64 keys (no key-range guards); otherwise P in {16, 32}.
@@ -96,24 +106,24 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
   const int lb = xcd * per + min(xcd, extra) + (b >> 3);
   const int wid = lb * 4 + wave;
   if (wid >= p.total_items) return;
+  const int rt = wid % p.n_rt;              // which 32-row tile of the group
   const int gid = wid / p.n_rt;
-  const int rt = wid - gid * p.n_rt;        // which 32-row tile of the group
-  const int h = gid / p.groups_per_head;
-  const int g0 = (gid - h * p.groups_per_head) * p.g;
-  const int gm = min(p.g, p.T - g0);
 
   unsigned char* wbase = smem + (size_t)wave * p.lds_wave;
   uint32_t* list = reinterpret_cast<uint32_t*>(wbase);        // page | members << 16
+  int h, gm, n_u = 0;
+  int my_t = -1, my_slot = -1;              // lane i < gm: member i's token (and slot)
+
+  if constexpr (MODE == kUnionMode) {
+  h = gid / p.groups_per_head;
+  const int g0 = (gid - h * p.groups_per_head) * p.g;
+  gm = min(p.g, p.T - g0);
   uint32_t* mask32 = reinterpret_cast<uint32_t*>(wbase + (size_t)p.n_umax * 4);
   const int n_mwords = (p.N + 3) >> 2;
-
-  // Members of the group (lane i < gm holds member i's token).
-  int my_t = -1;
   if (lane < gm) {
     const int t = p.ids[(size_t)h * p.T + g0 + lane];
     my_t = (t >= 0 && t < p.T) ? t : -1;
   }
-  int tmin = wave_min_u32(my_t >= 0 ? (uint32_t)my_t : 0xFFFFFFFFu);
 
   // ---- union + membership: mask byte per page, bit i = member i selected it
   for (int i = lane; i < n_mwords; i += 64) mask32[i] = 0;
@@ -140,7 +150,6 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
     }
   }
   wave_sync();
-  int n_u = 0;
   for (int c0 = 0; c0 < p.N; c0 += 64) {
     const int u = c0 + lane;
     const uint32_t m = (u < p.N) ? ((mask32[u >> 2] >> ((u & 3) * 8)) & 0xFFu) : 0u;
@@ -149,13 +158,36 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
     n_u += __popcll(bal);
   }
   wave_sync();
+  } else {
+  // entries [8 * tile, 8 * tile + 8) of the list of pair k of KV head h
+  const int tile = gid % p.tiles_per_pair;
+  const int hk = gid / p.tiles_per_pair;
+  h = hk / p.Np;
+  const int k = hk - h * p.Np;
+  const int cnt = p.pcount[hk];
+  gm = min(8, cnt - 8 * tile);
+  if (gm <= 0) return;
+  int kind = 0;
+  if (lane < gm) {
+    const int2 e = p.plist[(size_t)hk * p.Tc + 8 * tile + lane];
+    my_t = p.t0 + e.x;
+    my_slot = e.y & 0x3FFFFFFF;
+    kind = (e.y >> 30) & 3;                 // bit 0: page 2k selected, bit 1: page 2k+1
+  }
+  const uint32_t m0 = (uint32_t)__ballot(kind & 1) & 0xFFu;
+  const uint32_t m1 = (uint32_t)__ballot(kind & 2) & 0xFFu;
+  if (m0) list[n_u++] = (uint32_t)(2 * k) | (m0 << 16);
+  if (m1) list[n_u++] = (uint32_t)(2 * k + 1) | (m1 << 16);
+  wave_sync();
+  }
+  int tmin = wave_min_u32(my_t >= 0 ? (uint32_t)my_t : 0xFFFFFFFFu);
 
   // ---- per-lane query rows and Q operands (B of S^T = K Q^T).  Each bf16 row
   // is scaled by a power of two (absmax into [128, 256)) and split exactly into
   // two e4m3fn parts, hi + lo, so that K^T can run on the FP8 MFMA straight
   // from the cache bytes; 2^-e is folded back into the score scale.
   constexpr int KQ = D / 64;     // fp8 MFMA k-steps (64 d each, 32 per lane half)
-  int slot[NT], trow[NT], qhead[NT];
+  int slot[NT], trow[NT], qhead[NT], pslot[NT];
   float rscale[NT];
   i32x8 qhi[NT][KQ], qlo[NT][KQ];
 #pragma unroll
@@ -166,6 +198,7 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
     const bool ok = (s < gm) && (t >= 0);
     slot[nt] = ok ? s : -1;
     trow[nt] = ok ? t : -1;
+    pslot[nt] = __shfl(my_slot, s & 63);
     qhead[nt] = h * p.G + (n - s * p.G);
     const uint16_t* qp = p.Q + ((size_t)(ok ? t : 0) * p.Hq + qhead[nt]) * D + (D / 2) * hf;
     float q[D / 2];
@@ -420,6 +453,24 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
     }
   }
 
+  if constexpr (MODE == kPairMode) {
+    // ---- partials of the page pair: (m, l, acc) per owned row, merged later
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      const float l_tot = half_sum(l_run[nt]);
+      if (trow[nt] < 0) continue;
+      float* pp = p.partials + ((size_t)pslot[nt] * p.G + (qhead[nt] - h * p.G)) * (D + 4);
+      if (hf == 0) *reinterpret_cast<float2*>(pp) = make_float2(m_run[nt], l_tot);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          *reinterpret_cast<float4*>(pp + 4 + 32 * dt + 8 * rq + 4 * hf) =
+              make_float4(acc[nt][dt][4 * rq], acc[nt][dt][4 * rq + 1], acc[nt][dt][4 * rq + 2],
+                          acc[nt][dt][4 * rq + 3]);
+    }
+    return;
+  }
   // ---- epilogue: normalise and write each owned row once
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -446,14 +497,25 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
 #define PW_UA_PIPE 0   // 1: software-pipelined schedule at one wave per SIMD
 #endif
 
-template <int D>
+template <int D, int MODE>
 hipError_t launch_d(const UAParams& prm, int blocks, size_t lds, hipStream_t stream) {
   constexpr bool pipe = PW_UA_PIPE != 0;
   if (prm.P == 64)
-    hipLaunchKernelGGL((union_attn_kernel<D, true, pipe>), dim3(blocks), dim3(256), lds, stream, prm);
+    hipLaunchKernelGGL((union_attn_kernel<D, true, pipe, MODE>), dim3(blocks), dim3(256), lds,
+                       stream, prm);
   else
-    hipLaunchKernelGGL((union_attn_kernel<D, false, pipe>), dim3(blocks), dim3(256), lds, stream, prm);
+    hipLaunchKernelGGL((union_attn_kernel<D, false, pipe, MODE>), dim3(blocks), dim3(256), lds,
+                       stream, prm);
   return hipGetLastError();
+}
+
+void common_params(UAParams& prm, const pw_shape& s, const uint16_t* Q, const uint8_t* K,
+                   const uint8_t* V, const float* scales) {
+  prm = UAParams{};
+  prm.Q = Q; prm.K = K; prm.V = V; prm.scales = scales;
+  prm.T = s.T; prm.Hq = s.H_q; prm.Hkv = s.H_kv; prm.G = s.H_q / s.H_kv; prm.P = s.P;
+  prm.N = s.N_pages; prm.S = s.S;
+  prm.qk_scale = kLog2e / sqrtf((float)s.D);
 }
 
 }  // namespace
@@ -462,21 +524,39 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
                                   const uint8_t* V, const float* scales, const int32_t* sel,
                                   const int32_t* ids, int g, uint16_t* O, hipStream_t stream) {
   UAParams prm;
-  prm.Q = Q; prm.K = K; prm.V = V; prm.scales = scales; prm.sel = sel; prm.ids = ids; prm.O = O;
-  prm.T = s.T; prm.Hq = s.H_q; prm.Hkv = s.H_kv; prm.G = s.H_q / s.H_kv; prm.P = s.P;
-  prm.N = s.N_pages; prm.S = s.S; prm.g = g;
+  common_params(prm, s, Q, K, V, scales);
+  prm.sel = sel; prm.ids = ids; prm.O = O; prm.g = g;
   prm.groups_per_head = (s.T + g - 1) / g;
   prm.total_groups = prm.groups_per_head * s.H_kv;
   prm.n_umax = (g * s.S < s.N_pages) ? g * s.S : s.N_pages;
   const int mask_bytes = ((s.N_pages + 3) / 4) * 4;
   prm.lds_wave = ((prm.n_umax * 4 + mask_bytes) + 15) / 16 * 16;
-  prm.qk_scale = kLog2e / sqrtf((float)s.D);
   prm.n_rt = (g * prm.G + 31) / 32;
   prm.total_items = prm.total_groups * prm.n_rt;
   const int blocks = (prm.total_items + 3) / 4;
   const size_t lds = (size_t)prm.lds_wave * 4;
-  return s.D == 128 ? launch_d<128>(prm, blocks, lds, stream)
-                    : launch_d<64>(prm, blocks, lds, stream);
+  return s.D == 128 ? launch_d<128, kUnionMode>(prm, blocks, lds, stream)
+                    : launch_d<64, kUnionMode>(prm, blocks, lds, stream);
+}
+
+hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
+                                 const uint8_t* V, const float* scales, const int2* plist,
+                                 const int* pcount, float* partials, int Np, int Tc, int t0,
+                                 hipStream_t stream) {
+  UAParams prm;
+  common_params(prm, s, Q, K, V, scales);
+  prm.plist = plist; prm.pcount = pcount; prm.partials = partials;
+  prm.Np = Np; prm.Tc = Tc; prm.t0 = t0;
+  prm.g = 8;
+  prm.tiles_per_pair = (Tc + 7) / 8;
+  prm.n_rt = (8 * prm.G + 31) / 32;
+  prm.total_items = s.H_kv * Np * prm.tiles_per_pair * prm.n_rt;
+  prm.n_umax = 2;
+  prm.lds_wave = 16;
+  const int blocks = (prm.total_items + 3) / 4;
+  const size_t lds = (size_t)prm.lds_wave * 4;
+  return s.D == 128 ? launch_d<128, kPairMode>(prm, blocks, lds, stream)
+                    : launch_d<64, kPairMode>(prm, blocks, lds, stream);
 }
 
 }  // namespace pw
