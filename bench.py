@@ -151,14 +151,16 @@ def main():
     F_u = synth.useful_flops(inp["sel_pages"], wl)
 
     ids = pw.pw_group(shp, dev["sel_pages"], wl.W, wl.g)
+    ws = torch.empty(pw.pw_union_attention_workspace_bytes(shp, wl.g), dtype=torch.uint8,
+                     device="cuda")
     O = pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
-                              dev["sel_pages"], ids, wl.g)
+                              dev["sel_pages"], ids, wl.g, workspace=ws)
     torch.cuda.synchronize()
 
     def step():
         pw.pw_group(shp, dev["sel_pages"], wl.W, wl.g, query_ids=ids)
         pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
-                              dev["sel_pages"], ids, wl.g, O=O)
+                              dev["sel_pages"], ids, wl.g, O=O, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -172,7 +174,7 @@ def main():
         pw.pw_group(shp, dev["sel_pages"], wl.W, wl.g, query_ids=ids)
         e1.record(stream)
         pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
-                              dev["sel_pages"], ids, wl.g, O=O)
+                              dev["sel_pages"], ids, wl.g, O=O, workspace=ws)
         e2.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
@@ -232,12 +234,14 @@ def main():
             n = 5 if g_arm == 1 else 10
             for _ in range(2):
                 pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"],
-                                      dev["scales"], dev["sel_pages"], ids_arm, g_arm, O=O)
+                                      dev["scales"], dev["sel_pages"], ids_arm, g_arm, O=O,
+                                      workspace=ws)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record(stream)
             for _ in range(n):
                 pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"],
-                                      dev["scales"], dev["sel_pages"], ids_arm, g_arm, O=O)
+                                      dev["scales"], dev["sel_pages"], ids_arm, g_arm, O=O,
+                                      workspace=ws)
             b.record(stream)
             torch.cuda.synchronize()
             ms = a.elapsed_time(b) / n

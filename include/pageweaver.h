@@ -137,8 +137,13 @@ pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W,
  *      query_ids row that is not a permutation leaves unlisted rows of O
  *      unwritten.
  * Out: O.
- * Support set: D in {64, 128}; P in {16, 32, 64}; N_pages <= 32768.
- * Workspace: none (returns 0).
+ * Support set: D in {64, 128}; P in {16, 32, 64}; N_pages <= 32768; the
+ * re-tiled K (and V) copy below at most 2 GiB.
+ * Workspace: pw_union_attention_workspace_bytes() = 2 * N_pages * H_kv * 64 * D
+ * bytes, 256-byte aligned, required.  Each call first re-tiles the FP8 K and V
+ * pages into it in matrix-core operand order (64 key slots per page, keys
+ * >= P zero), so that every page load of the attention loop is a contiguous
+ * 1 KB wave read; its contents are rebuilt by every call.
  * ------------------------------------------------------------------------- */
 size_t pw_union_attention_workspace_bytes(const pw_shape* shape, int32_t g);
 pw_status pw_union_attention(const pw_shape* shape, const uint16_t* Q,
@@ -164,8 +169,8 @@ pw_status pw_union_attention(const pw_shape* shape, const uint16_t* Q,
  * pw_union_attention up to floating-point order.
  *
  * In/Out/support: as pw_union_attention (no query_ids), plus G <= 8 and
- * N_pages <= 4096; queries are processed in chunks sized so that the
- * workspace stays within about 4 GiB.
+ * N_pages <= 4096; queries are processed in chunks sized so that the partial
+ * outputs stay within about 4 GiB of workspace (plus the re-tiled K/V copy).
  * Workspace: pw_dense_union_ref_workspace_bytes(shape) bytes, 256-byte
  * aligned.
  * ------------------------------------------------------------------------- */

@@ -91,22 +91,29 @@ pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W, i
                     "pw_group launch");
 }
 
-size_t pw_union_attention_workspace_bytes(const pw_shape*, int32_t) { return 0; }
+size_t pw_union_attention_workspace_bytes(const pw_shape* shape, int32_t) {
+  if (check_shape(shape) != PW_OK) return 0;
+  return pw::tiled_kv_bytes(*shape);
+}
 
 pw_status pw_union_attention(const pw_shape* shape, const uint16_t* Q, const uint8_t* K_fp8,
                              const uint8_t* V_fp8, const float* scales, const int32_t* sel_pages,
                              const int32_t* query_ids, int32_t g, uint16_t* O, void* ws,
                              size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   pw_status st = check_shape(shape);
   if (st != PW_OK) return st;
   if (!Q || !K_fp8 || !V_fp8 || !scales || !sel_pages || !query_ids || !O)
     return fail(PW_ERR_NULL, "Q, K_fp8, V_fp8, scales, sel_pages, query_ids and O are required");
   st = check_attention_support(shape, g);
   if (st != PW_OK) return st;
+  const size_t need = pw::tiled_kv_bytes(*shape);
+  if (!ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
+  if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (((uintptr_t)ws & 255) != 0) return fail(PW_ERR_DIMS, "workspace must be 256-byte aligned");
+  if (need / 2 > 0x7FFFFFFFu)
+    return fail(PW_ERR_UNSUPPORTED, "tiled K/V of %zu bytes exceeds 2 GiB", need / 2);
   return hip_status(pw::launch_union_attention(*shape, Q, K_fp8, V_fp8, scales, sel_pages,
-                                               query_ids, g, O, (hipStream_t)stream),
+                                               query_ids, g, O, ws, (hipStream_t)stream),
                     "pw_union_attention launch");
 }
 

@@ -6,7 +6,8 @@
 // summary": it works on disjoint page pairs and uses the full membership of
 // each page to form common or exclusive query lists.
 //
-// Per chunk of Tc queries (all KV heads), on the caller's stream:
+// The FP8 pages are first re-tiled in MFMA operand order (as for the query
+// union).  Then per chunk of Tc queries (all KV heads), on the caller's stream:
 //   1. zero the per-pair list lengths;
 //   2. pair_entries_kernel: one thread per (KV head, query) sets its page
 //      bitset in LDS, walks its pairs (2k, 2k+1) in ascending order and appends
@@ -29,7 +30,7 @@ constexpr size_t kBudget = size_t(4) << 30;   // workspace bound (bytes)
 
 struct DUPlan {
   int Np, maxp, Tc, NW;
-  size_t off_count, off_npairs, off_list, off_part, total;
+  size_t off_tiles, off_count, off_npairs, off_list, off_part, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -47,8 +48,9 @@ DUPlan plan(const pw_shape& s) {
   const size_t tmax = ((size_t)s.T + 63) / 64 * 64;
   if (tc > tmax) tc = tmax;
   d.Tc = (int)tc;
-  d.off_count = 0;
-  d.off_npairs = align256((size_t)s.H_kv * d.Np * 4);
+  d.off_tiles = 0;
+  d.off_count = align256(tiled_kv_bytes(s));
+  d.off_npairs = d.off_count + align256((size_t)s.H_kv * d.Np * 4);
   d.off_list = d.off_npairs + align256((size_t)s.H_kv * d.Tc * 4);
   d.off_part = d.off_list + align256((size_t)s.H_kv * d.Np * d.Tc * 8);
   d.total = d.off_part + align256((size_t)s.H_kv * d.Tc * d.maxp * G * (s.D + 4) * 4);
@@ -145,6 +147,9 @@ hipError_t launch_dense_union(const pw_shape& s, const uint16_t* Q, const uint8_
   int2* plist = reinterpret_cast<int2*>(base + d.off_list);
   float* partials = reinterpret_cast<float*>(base + d.off_part);
   const int G = s.H_q / s.H_kv;
+  uint8_t* tiles = reinterpret_cast<uint8_t*>(base + d.off_tiles);
+  hipError_t e0 = tile_kv(s, K, V, tiles, stream);
+  if (e0 != hipSuccess) return e0;
   for (int t0 = 0; t0 < s.T; t0 += d.Tc) {
     const int n_count = s.H_kv * d.Np;
     hipLaunchKernelGGL(zero_kernel, dim3((n_count + 255) / 256), dim3(256), 0, stream, pcount,
@@ -155,7 +160,7 @@ hipError_t launch_dense_union(const pw_shape& s, const uint16_t* Q, const uint8_
                        d.Tc, d.maxp, t0, pcount, npairs, plist);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_pair_attention(s, Q, K, V, scales, plist, pcount, partials, d.Np, d.Tc, t0, stream);
+    e = launch_pair_attention(s, Q, tiles, scales, plist, pcount, partials, d.Np, d.Tc, t0, stream);
     if (e != hipSuccess) return e;
     if (s.D == 128)
       hipLaunchKernelGGL(merge_kernel<128>, dim3(tcur, s.H_kv), dim3(64), 0, stream, partials,

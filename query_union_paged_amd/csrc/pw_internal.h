@@ -52,13 +52,17 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
 // Host-side launchers (implemented next to their kernels).
 hipError_t launch_group(const pw_shape& s, const int32_t* sel, int W, int g, int32_t* ids,
                         hipStream_t stream);
+// FP8 K/V pages re-tiled in MFMA operand order (K tiles, then V tiles).
+size_t tiled_kv_bytes(const pw_shape& s);
+hipError_t tile_kv(const pw_shape& s, const uint8_t* K, const uint8_t* V, uint8_t* tiles,
+                   hipStream_t stream);
 hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
                                   const uint8_t* V, const float* scales, const int32_t* sel,
-                                  const int32_t* ids, int g, uint16_t* O, hipStream_t stream);
-hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
-                                 const uint8_t* V, const float* scales, const int2* plist,
-                                 const int* pcount, float* partials, int Np, int Tc, int t0,
-                                 hipStream_t stream);
+                                  const int32_t* ids, int g, uint16_t* O, void* ws,
+                                  hipStream_t stream);
+hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* tiles,
+                                 const float* scales, const int2* plist, const int* pcount,
+                                 float* partials, int Np, int Tc, int t0, hipStream_t stream);
 size_t dense_union_workspace(const pw_shape& s);
 hipError_t launch_dense_union(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
                               const uint8_t* V, const float* scales, const int32_t* sel,

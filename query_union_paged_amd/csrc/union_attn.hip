@@ -29,6 +29,13 @@
 // once, by its wave.  There are no atomics and no partial outputs.
 #include "pw_internal.h"
 
+#ifndef PW_UA_PIPE
+#define PW_UA_PIPE 0      // 1: software-pipelined schedule at one wave per SIMD
+#endif
+#ifndef PW_UA_WG_WAVES
+#define PW_UA_WG_WAVES 4  // waves (independent groups) per workgroup
+#endif
+
 namespace pw {
 namespace {
 
@@ -39,6 +46,8 @@ struct UAParams {
   const uint16_t* Q;
   const uint8_t* K;
   const uint8_t* V;
+  const uint8_t* Kt;   // tiled copies (see tile_kv_kernel)
+  const uint8_t* Vt;
   const float* scales;
   const int32_t* sel;
   const int32_t* ids;
@@ -81,11 +90,45 @@ __device__ __forceinline__ uint4 load16(const uint8_t* p) {
   return *reinterpret_cast<const uint4*>(p);
 }
 
+// Re-tiles the FP8 pages of one layer into MFMA operand order (one workgroup
+// per (page, KV head) block of 64 key slots x D bytes, for K and for V):
+//   K chunk (kt, c, l) = K[tile_key(l % 32, kt)][(D/2)(l/32) + 16c .. +16)
+//   V chunk (dt, j, l) = V[32 dt + l % 32][32 (l/32) + 16 j .. +16)   (dim-major page)
+// at byte 16 * ((kt * D/32 + c) * 64 + l), resp. 16 * ((2 dt + j) * 64 + l);
+// key slots >= P are zero.  The attention loop then reads each page with
+// contiguous 1 KB wave loads instead of one 128-byte row per lane.
+template <int D>
+__global__ __launch_bounds__(256) void tile_kv_kernel(const uint8_t* __restrict__ K,
+                                                      const uint8_t* __restrict__ V,
+                                                      uint8_t* __restrict__ Kt,
+                                                      uint8_t* __restrict__ Vt, int P) {
+  constexpr int KCH = D / 32, DT = D / 32;
+  const size_t blk = blockIdx.x;                   // page * H_kv + head
+  const uint8_t* kp = K + blk * P * D;
+  const uint8_t* vp = V + blk * D * P;
+  uint8_t* kt_out = Kt + blk * 64 * D;
+  uint8_t* vt_out = Vt + blk * 64 * D;
+  for (int q = threadIdx.x; q < 2 * KCH * 64; q += blockDim.x) {
+    const int l = q & 63, kc = q >> 6, kt = kc / KCH, c = kc - kt * KCH;
+    const int key = tile_key(l & 31, kt);
+    const uint4 v = (key < P) ? load16(kp + (size_t)key * D + (D / 2) * (l >> 5) + 16 * c)
+                              : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(kt_out + 16 * q) = v;
+  }
+  for (int q = threadIdx.x; q < 2 * DT * 64; q += blockDim.x) {
+    const int l = q & 63, dj = q >> 6, dt = dj >> 1, j = dj & 1;
+    const int k0 = 32 * (l >> 5) + 16 * j;
+    const uint4 v = (k0 < P) ? load16(vp + (size_t)(32 * dt + (l & 31)) * P + k0)
+                             : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(vt_out + 16 * q) = v;
+  }
+}
+
 // MODE kUnionMode: groups of query IDs, union of their selected pages, O out.
 // MODE kPairMode: up to 8 entries of one page pair's membership list, the pair's
 // pages they selected, unnormalised partials out (direct KV-page union).
 template <int D, bool P64, bool PIPE, int MODE>
-__global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams p) {
+__global__ __launch_bounds__(64 * PW_UA_WG_WAVES, PIPE ? 1 : 2) void union_attn_kernel(UAParams p) {
   constexpr int NT = 1;          // one 32-row tile per wave
   // P64: pages of exactly 64 keys (no key-range guards); otherwise P in {16, 32}.
   const int P = P64 ? 64 : p.P;
@@ -104,7 +147,7 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
   const int nb = gridDim.x, b = blockIdx.x;
   const int xcd = b & 7, per = nb >> 3, extra = nb & 7;
   const int lb = xcd * per + min(xcd, extra) + (b >> 3);
-  const int wid = lb * 4 + wave;
+  const int wid = lb * PW_UA_WG_WAVES + wave;
   if (wid >= p.total_items) return;
   const int rt = wid % p.n_rt;              // which 32-row tile of the group
   const int gid = wid / p.n_rt;
@@ -254,43 +297,39 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
       for (int r = 0; r < 16; ++r) acc[nt][dt][r] = 0.f;
   }
 
-  const size_t page_stride = (size_t)p.Hkv * P * D;     // bytes between pages
-  const uint8_t* kbase = p.K + (size_t)h * P * D;
-  const uint8_t* vbase = p.V + (size_t)h * D * P;
-  int krow[2];
-#pragma unroll
-  for (int kt = 0; kt < 2; ++kt) krow[kt] = tile_key(col, kt);
-  const int vbytes = min(max(P - 32 * hf, 0), 32);     // valid V bytes of this lane's row
-
-  // Two pages in flight.  Step `up` (buffer c = up & 1, n = c ^ 1):
-  //   prefetch K(up+2) into kbuf[c]      (K(up) was consumed by QK(up))
-  //   QK(up+1) on kbuf[n] -> sacc[n]     (matrix cores ...
-  //   softmax(up) on sacc[c]             ... while the VALU works on page up)
-  //   PV(up) with vbuf[c] -> acc
-  //   prefetch V(up+2) into vbuf[c]
-  // Loads past the last page re-read the last page (one redundant page per
-  // group keeps the prefetch unconditional).
+  // K and V come from the tiled copies (tile_kv_kernel): the block of (page u,
+  // KV head h) holds 64 key slots x D in MFMA operand order, so every load
+  // below is one contiguous 1 KB read of the wave (lane l at 16 * l).
   uint4 kbuf[2][2][KCH], vbuf[2][DT][2];
   f32x16 sacc[2][NT][2];
   float ksr[2], vsr[2];
   auto page_of = [&](int i) { return (int)(list[min(i, n_u - 1)] & 0xFFFF); };
+  const int block_bytes = 64 * D;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.Kt, (short)0, 0x7FFFFFFF, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)p.Vt, (short)0, 0x7FFFFFFF, 0x00020000);
+  const int loff = 16 * lane;
+  auto block_of = [&](int u) {
+    return (__builtin_amdgcn_readfirstlane(u) * p.Hkv + h) * block_bytes;
+  };
   auto load_k = [&](uint4 (&kr)[2][KCH], int u) {
-    const uint8_t* kp = kbase + (size_t)u * page_stride + (D / 2) * hf;
+    const int so = block_of(u);
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int c = 0; c < KCH; ++c)
-        kr[kt][c] = (P64 || krow[kt] < P) ? load16(kp + (size_t)krow[kt] * D + 16 * c)
-                                          : make_uint4(0, 0, 0, 0);
+        kr[kt][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  krs, loff + 1024 * (kt * KCH + c), so, 0));
   };
   auto load_v = [&](uint4 (&vr)[DT][2], int u) {
-    const uint8_t* vp = vbase + (size_t)u * page_stride + 32 * hf;
+    const int so = block_of(u);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const uint8_t* row = vp + (size_t)(32 * dt + col) * P;
-      vr[dt][0] = (P64 || vbytes >= 16) ? load16(row) : make_uint4(0, 0, 0, 0);
-      vr[dt][1] = (P64 || vbytes >= 32) ? load16(row + 16) : make_uint4(0, 0, 0, 0);
-    }
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        vr[dt][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                  vrs, loff + 1024 * (2 * dt + j), so, 0));
   };
   const float* kscale = p.scales + h;                       // [N][Hkv]
   const float* vscale = p.scales + (size_t)p.N * p.Hkv + h;
@@ -321,13 +360,10 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
     }
   };
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-  // mask, online softmax (log2 domain, v_scale folded into the exponent), PV
-  auto softmax_pv = [&](f32x16 (&sc)[NT][2], const uint4 (&vr)[DT][2], int u, uint32_t mbits,
-                        float ks_raw, float vs_raw) {
-    const float ksc0 = ks_raw * p.qk_scale;
-    const float lvs = __builtin_amdgcn_logf(vs_raw);    // log2
-    const float ivs = __builtin_amdgcn_rcpf(vs_raw);
-    // causal / page-size mask, only where some key can lie after a member
+
+  // ---- stages of one page: mask -> softmax -> (rescale) -> PV
+  // causal / page-size mask, only where some key can lie after a member
+  auto mask_page = [&](f32x16 (&sc)[NT][2], int u) {
     const bool need_mask = !P64 || (u * P + P - 1 > tmin);
     if (need_mask) {
 #pragma unroll
@@ -340,7 +376,15 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
             if ((!P64 && key >= P) || u * P + key > trow[nt]) sc[nt][kt][r] = -INFINITY;
           }
     }
-    bf16x8 pB[NT][4];
+  };
+  // online softmax in the log2 domain, v_scale folded into the exponent; the
+  // probabilities are produced as bf16 MFMA operands; returns the rescale
+  // factor of the accumulator (1 unless the reference max moved)
+  auto softmax = [&](f32x16 (&sc)[NT][2], uint32_t mbits, float ks_raw, float vs_raw,
+                     bf16x8 (&pB)[NT][4], float (&alph)[NT]) {
+    const float ksc0 = ks_raw * p.qk_scale;
+    const float lvs = __builtin_amdgcn_logf(vs_raw);    // log2
+    const float ivs = __builtin_amdgcn_rcpf(vs_raw);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       float mx = -INFINITY;
@@ -353,7 +397,8 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
       const float ksc = ksc0 * rscale[nt];
       const float mx2 = mx * ksc;
       const float m_new = (member && mx2 > m_run[nt] + kTau) ? mx2 : m_run[nt];
-      const float alpha = (m_new == m_run[nt]) ? 1.f : __builtin_amdgcn_exp2f(m_run[nt] - m_new);
+      // branch-free: exp2(0) = 1 exactly when the reference max is unchanged
+      const float alpha = __builtin_amdgcn_exp2f((m_new == m_run[nt]) ? 0.f : m_run[nt] - m_new);
       m_run[nt] = m_new;
       const float bias = (member && m_new > -INFINITY) ? (lvs - m_new) : -INFINITY;
       float ps = 0.f;
@@ -374,14 +419,22 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
         pB[nt][q] = v;
       }
       l_run[nt] = l_run[nt] * alpha + ps * ivs;
-      if (__ballot(alpha != 1.f)) {
+      alph[nt] = alpha;
+    }
+  };
+  auto rescale = [&](const float (&alph)[NT]) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      if (__ballot(alph[nt] != 1.f)) {
 #pragma unroll
         for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) acc[nt][dt][r] *= alpha;
+          for (int r = 0; r < 16; ++r) acc[nt][dt][r] *= alph[nt];
       }
     }
-    // O^T += V^T P^T  (d tiles innermost: consecutive MFMAs are independent)
+  };
+  // O^T += V^T P^T  (d tiles innermost: consecutive MFMAs are independent)
+  auto pv = [&](const uint4 (&vr)[DT][2], const bf16x8 (&pB)[NT][4]) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
 #pragma unroll
@@ -396,35 +449,60 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
   };
 
   if (PIPE) {
-    // QK(up+1) on the matrix cores overlaps softmax(up) on the VALU; K and V
-    // are fetched two pages ahead (one wave per SIMD, 512 registers).
+    // Three-stage software pipeline, one wave per SIMD.  Iteration u runs
+    // PV(u-1), softmax(u) and QK(u+1) in one basic block (independent work for
+    // the matrix cores and the VALU), after the rarely taken rescale and mask
+    // branches.  K is fetched 2 pages ahead, V one page ahead of its use.
+    // K(x), V(x), S(x), P(x) live in buffer x & 1.
+    bf16x8 pbuf[2][NT][4];
+    float alph[NT];
     if (n_u > 0) {
-      const int u0 = page_of(0), u1 = page_of(1);
-      load_k(kbuf[0], u0);
-      load_v(vbuf[0], u0);
-      load_k(kbuf[1], u1);
-      load_v(vbuf[1], u1);
-      ksr[0] = kscale[(size_t)u0 * p.Hkv];
-      vsr[0] = vscale[(size_t)u0 * p.Hkv];
-      ksr[1] = kscale[(size_t)u1 * p.Hkv];
-      vsr[1] = vscale[(size_t)u1 * p.Hkv];
+      load_k(kbuf[0], page_of(0));
+      load_k(kbuf[1], page_of(1));
+      load_v(vbuf[0], page_of(0));
+      load_v(vbuf[1], page_of(1));
+      ksr[0] = kscale[(size_t)page_of(0) * p.Hkv];
+      vsr[0] = vscale[(size_t)page_of(0) * p.Hkv];
+      ksr[1] = kscale[(size_t)page_of(1) * p.Hkv];
+      vsr[1] = vscale[(size_t)page_of(1) * p.Hkv];
       qk(kbuf[0], sacc[0]);
+      load_k(kbuf[0], page_of(2));
+      // iteration 0: no PV yet
+      const uint32_t ent = list[0];
+      mask_page(sacc[0], ent & 0xFFFF);
+      softmax(sacc[0], ent >> 16, ksr[0], vsr[0], pbuf[0], alph);
+      ksr[0] = kscale[(size_t)page_of(2) * p.Hkv];
+      vsr[0] = vscale[(size_t)page_of(2) * p.Hkv];
+      qk(kbuf[1], sacc[1]);
+      load_k(kbuf[1], page_of(3));
     }
-    for (int up0 = 0; up0 < n_u; up0 += 2) {
+    for (int u0 = 1; u0 < n_u + 1; u0 += 2) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const int up = up0 + c;
-        if (up < n_u) {
-          const int n = c ^ 1;
-          const uint32_t ent = list[up];
-          const float ks_c = ksr[c], vs_c = vsr[c];
-          const int u2 = page_of(up + 2);
-          load_k(kbuf[c], u2);
-          ksr[c] = kscale[(size_t)u2 * p.Hkv];
-          vsr[c] = vscale[(size_t)u2 * p.Hkv];
-          if (up + 1 < n_u) qk(kbuf[n], sacc[n]);
-          softmax_pv(sacc[c], vbuf[c], ent & 0xFFFF, ent >> 16, ks_c, vs_c);
-          load_v(vbuf[c], u2);
+      for (int c = 0; c < 2; ++c) {      // page u has parity c ^ 1 (u0 is odd)
+        const int u = u0 + c;
+        const int pc = c ^ 1, pp = c;    // buffers of page u and page u - 1
+        if (u < n_u) {
+          rescale(alph);
+          const uint32_t ent = list[u];
+          mask_page(sacc[pc], ent & 0xFFFF);
+          const float ks_c = ksr[pc], vs_c = vsr[pc];
+          pv(vbuf[pp], pbuf[pp]);
+          softmax(sacc[pc], ent >> 16, ks_c, vs_c, pbuf[pc], alph);
+          qk(kbuf[pp], sacc[pp]);        // page u + 1 (past the end: recomputes the last page)
+          if (PIPE) {
+#pragma unroll
+            for (int i = 0; i < 24; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
+            }
+          }
+          load_v(vbuf[pp], page_of(u + 1));
+          load_k(kbuf[pp], page_of(u + 3));
+          ksr[pc] = kscale[(size_t)page_of(u + 2) * p.Hkv];
+          vsr[pc] = vscale[(size_t)page_of(u + 2) * p.Hkv];
+        } else if (u == n_u) {
+          rescale(alph);
+          pv(vbuf[pp], pbuf[pp]);        // the last page's PV
         }
       }
     }
@@ -438,6 +516,8 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
       ksr[0] = kscale[(size_t)u0 * p.Hkv];
       vsr[0] = vscale[(size_t)u0 * p.Hkv];
     }
+    bf16x8 pB[NT][4];
+    float alph[NT];
     for (int up = 0; up < n_u; ++up) {
       const uint32_t ent = list[up];
       const float ks_c = ksr[0], vs_c = vsr[0];
@@ -447,7 +527,10 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
       load_k(kbuf[0], u1);
       ksr[0] = kscale[(size_t)u1 * p.Hkv];
       vsr[0] = vscale[(size_t)u1 * p.Hkv];
-      softmax_pv(sacc[0], vbuf[0], ent & 0xFFFF, ent >> 16, ks_c, vs_c);
+      mask_page(sacc[0], ent & 0xFFFF);
+      softmax(sacc[0], ent >> 16, ks_c, vs_c, pB, alph);
+      rescale(alph);
+      pv(vbuf[0], pB);
       __builtin_amdgcn_sched_barrier(0);
       load_v(vbuf[0], u1);
     }
@@ -493,19 +576,16 @@ __global__ __launch_bounds__(256, PIPE ? 1 : 2) void union_attn_kernel(UAParams 
   }
 }
 
-#ifndef PW_UA_PIPE
-#define PW_UA_PIPE 0   // 1: software-pipelined schedule at one wave per SIMD
-#endif
 
 template <int D, int MODE>
 hipError_t launch_d(const UAParams& prm, int blocks, size_t lds, hipStream_t stream) {
   constexpr bool pipe = PW_UA_PIPE != 0;
   if (prm.P == 64)
-    hipLaunchKernelGGL((union_attn_kernel<D, true, pipe, MODE>), dim3(blocks), dim3(256), lds,
-                       stream, prm);
+    hipLaunchKernelGGL((union_attn_kernel<D, true, pipe, MODE>), dim3(blocks),
+                       dim3(64 * PW_UA_WG_WAVES), lds, stream, prm);
   else
-    hipLaunchKernelGGL((union_attn_kernel<D, false, pipe, MODE>), dim3(blocks), dim3(256), lds,
-                       stream, prm);
+    hipLaunchKernelGGL((union_attn_kernel<D, false, pipe, MODE>), dim3(blocks),
+                       dim3(64 * PW_UA_WG_WAVES), lds, stream, prm);
   return hipGetLastError();
 }
 
@@ -520,11 +600,31 @@ void common_params(UAParams& prm, const pw_shape& s, const uint16_t* Q, const ui
 
 }  // namespace
 
+size_t tiled_kv_bytes(const pw_shape& s) { return (size_t)2 * s.N_pages * s.H_kv * 64 * s.D; }
+
+hipError_t tile_kv(const pw_shape& s, const uint8_t* K, const uint8_t* V, uint8_t* tiles,
+                   hipStream_t stream) {
+  uint8_t* Kt = tiles;
+  uint8_t* Vt = tiles + tiled_kv_bytes(s) / 2;
+  const dim3 grid(s.N_pages * s.H_kv);
+  if (s.D == 128)
+    hipLaunchKernelGGL(tile_kv_kernel<128>, grid, dim3(256), 0, stream, K, V, Kt, Vt, s.P);
+  else
+    hipLaunchKernelGGL(tile_kv_kernel<64>, grid, dim3(256), 0, stream, K, V, Kt, Vt, s.P);
+  return hipGetLastError();
+}
+
 hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
                                   const uint8_t* V, const float* scales, const int32_t* sel,
-                                  const int32_t* ids, int g, uint16_t* O, hipStream_t stream) {
+                                  const int32_t* ids, int g, uint16_t* O, void* ws,
+                                  hipStream_t stream) {
+  uint8_t* tiles = static_cast<uint8_t*>(ws);
+  hipError_t e = tile_kv(s, K, V, tiles, stream);
+  if (e != hipSuccess) return e;
   UAParams prm;
   common_params(prm, s, Q, K, V, scales);
+  prm.Kt = tiles;
+  prm.Vt = tiles + tiled_kv_bytes(s) / 2;
   prm.sel = sel; prm.ids = ids; prm.O = O; prm.g = g;
   prm.groups_per_head = (s.T + g - 1) / g;
   prm.total_groups = prm.groups_per_head * s.H_kv;
@@ -533,18 +633,19 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
   prm.lds_wave = ((prm.n_umax * 4 + mask_bytes) + 15) / 16 * 16;
   prm.n_rt = (g * prm.G + 31) / 32;
   prm.total_items = prm.total_groups * prm.n_rt;
-  const int blocks = (prm.total_items + 3) / 4;
-  const size_t lds = (size_t)prm.lds_wave * 4;
+  const int blocks = (prm.total_items + PW_UA_WG_WAVES - 1) / PW_UA_WG_WAVES;
+  const size_t lds = (size_t)prm.lds_wave * PW_UA_WG_WAVES;
   return s.D == 128 ? launch_d<128, kUnionMode>(prm, blocks, lds, stream)
                     : launch_d<64, kUnionMode>(prm, blocks, lds, stream);
 }
 
-hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
-                                 const uint8_t* V, const float* scales, const int2* plist,
-                                 const int* pcount, float* partials, int Np, int Tc, int t0,
-                                 hipStream_t stream) {
+hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* tiles,
+                                 const float* scales, const int2* plist, const int* pcount,
+                                 float* partials, int Np, int Tc, int t0, hipStream_t stream) {
   UAParams prm;
-  common_params(prm, s, Q, K, V, scales);
+  common_params(prm, s, Q, nullptr, nullptr, scales);
+  prm.Kt = tiles;
+  prm.Vt = tiles + tiled_kv_bytes(s) / 2;
   prm.plist = plist; prm.pcount = pcount; prm.partials = partials;
   prm.Np = Np; prm.Tc = Tc; prm.t0 = t0;
   prm.g = 8;
@@ -553,8 +654,8 @@ hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uin
   prm.total_items = s.H_kv * Np * prm.tiles_per_pair * prm.n_rt;
   prm.n_umax = 2;
   prm.lds_wave = 16;
-  const int blocks = (prm.total_items + 3) / 4;
-  const size_t lds = (size_t)prm.lds_wave * 4;
+  const int blocks = (prm.total_items + PW_UA_WG_WAVES - 1) / PW_UA_WG_WAVES;
+  const size_t lds = (size_t)prm.lds_wave * PW_UA_WG_WAVES;
   return s.D == 128 ? launch_d<128, kPairMode>(prm, blocks, lds, stream)
                     : launch_d<64, kPairMode>(prm, blocks, lds, stream);
 }

@@ -112,8 +112,13 @@ def pw_group(shp: PWShape, sel_pages: torch.Tensor, W: int, g: int,
     return query_ids
 
 
+def pw_union_attention_workspace_bytes(shp: PWShape, g: int = 8) -> int:
+    return int(_lib.pw_union_attention_workspace_bytes(ctypes.byref(shp), g))
+
+
 def pw_union_attention(shp: PWShape, Q, K_fp8, V_fp8, scales, sel_pages, query_ids, g: int,
-                       O: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                       O: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                       stream=None) -> torch.Tensor:
     T, Hq, Hkv, D, P, N, S = shp.T, shp.H_q, shp.H_kv, shp.D, shp.P, shp.N_pages, shp.S
     q = _dev(Q, "Q", _BF16, (T, Hq, D))
     k = _dev(K_fp8, "K_fp8", _U8, (N, Hkv, P, D))
@@ -124,8 +129,12 @@ def pw_union_attention(shp: PWShape, Q, K_fp8, V_fp8, scales, sel_pages, query_i
     if O is None:
         O = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=Q.device)
     o = _dev(O, "O", _BF16, (T, Hq, D))
-    _check(_lib.pw_union_attention(ctypes.byref(shp), q, k, v, sc, sel, ids, g, o, None, 0,
-                                   _stream(stream)), "pw_union_attention")
+    if workspace is None:
+        workspace = torch.empty(pw_union_attention_workspace_bytes(shp, g), dtype=torch.uint8,
+                                device=Q.device)
+    ws = _dev(workspace, "workspace", (torch.uint8,))
+    _check(_lib.pw_union_attention(ctypes.byref(shp), q, k, v, sc, sel, ids, g, o, ws,
+                                   workspace.numel(), _stream(stream)), "pw_union_attention")
     return O
 
 

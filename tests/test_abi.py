@@ -71,7 +71,13 @@ def test_attention_validation():
     assert _attn(_shape(S=200), g=8) == pw.PW_ERR_UNSUPPORTED           # g * S > 1024
     assert _attn(_shape(N_pages=65536, T=65536 * 16)) == pw.PW_ERR_UNSUPPORTED
     assert _attn(_shape(S=-1)) == pw.PW_ERR_DIMS
-    assert pw._lib.pw_union_attention_workspace_bytes(ctypes.byref(_shape()), 8) == 0
+    shp = _shape()
+    need = pw._lib.pw_union_attention_workspace_bytes(ctypes.byref(shp), 8)
+    assert need == 2 * 64 * 1 * 64 * 64
+    f = pw._lib.pw_union_attention
+    assert f(ctypes.byref(shp), *[FAKE] * 6, 8, FAKE, None, need, None) == pw.PW_ERR_NULL
+    assert f(ctypes.byref(shp), *[FAKE] * 6, 8, FAKE, FAKE, need - 1, None) == pw.PW_ERR_WORKSPACE
+    assert f(ctypes.byref(shp), *[FAKE] * 6, 8, FAKE, ctypes.c_void_p(0x1010), need, None) == pw.PW_ERR_DIMS
 
 
 def test_dense_union_validation():
