@@ -7,19 +7,22 @@
 // sets add few new pages; g is fixed independently of the window W.
 //
 // One wave per (KV head, aligned window).  Lane l owns candidates l, l+64,
-// l+128, ... (C = ceil(W/64) of them) and keeps their page bitsets in VGPRs;
-// the group union U is wave-uniform and lives in scalar registers.  A step is
-// a wave minimum of key = (cost << 10 | local index) over the available
-// candidates (DPP within rows of 16, then four readlanes), so the lowest
-// index wins ties and the result is bit-exact.  The winner's words are read
-// with readlane from the owning lane; only the words where the winner brings
-// new pages (delta = B_best & ~U) touch the candidates' costs.
+// l+128, ... (C = ceil(W/64) of them) and keeps their page bitsets in VGPRs,
+// compacted to the words the window uses; the bitsets are built 64
+// candidates at a time in LDS from 16-byte loads of the selection rows.  A
+// step is a wave minimum of key = (cost << 10 | local index) over the
+// available candidates (DPP within rows of 16, then four readlanes), so the
+// lowest index wins ties and the result is bit-exact.  The winner's words
+// come to scalar registers by readlane; only the words where it brings new
+// pages (delta = B_best & ~U) touch the candidates, whose cost is kept as
+// |B_c| - |B_c & U| with |B_c & U| accumulated popcount by popcount.
 #include "pw_internal.h"
 
 namespace pw {
 namespace {
 
 constexpr uint32_t kNone = 0xFFFFFFFFu;
+constexpr int kStride = 33;   // LDS words per candidate bitset (32 + 1 pad: conflict-free rows)
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_min(uint32_t v) {
@@ -47,42 +50,90 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
          __builtin_amdgcn_readlane(v, 32) | __builtin_amdgcn_readlane(v, 48);
 }
 
-// The greedy loop of one window, with the window's active words compacted into
-// NWB register words per candidate (NWB >= number of active words; the words
-// past it are zero for every candidate and cost nothing).
+// The greedy loop of one window.  The window's bitsets are staged 64
+// candidates at a time (LDS `stage`) and kept in registers compacted to the
+// window's active words (word jj = the jj-th word any candidate uses; words
+// past the active count are zero for every candidate and cost nothing).
 template <int C, int NWB>
 __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, int S, int N,
                                             int Wr, int g, uint32_t act, uint32_t* stage,
                                             int* order) {
-  constexpr int STR = NWB + 1;             // padded row: conflict-free column reads
   const int lane = threadIdx.x;
   uint32_t b[C][NWB];
-#pragma unroll
-  for (int c = 0; c < C; ++c) {
-    for (int i = lane; i < 64 * STR; i += 64) stage[i] = 0;
+  // one 64-candidate chunk: bits set in LDS, then each lane takes its row
+  auto build_chunk = [&](uint32_t(&bc)[NWB], const int c) __attribute__((always_inline)) {
+    for (int i = lane; i < 64 * kStride; i += 64) stage[i] = 0;
     wave_sync();
     const int r0 = 64 * c;
     const int nrows = max(0, min(64, Wr - r0));
     const int32_t* base = wbase + (size_t)r0 * S;
-    for (int i = lane; i < nrows * S; i += 64) {
-      const int u = base[i];
-      if (u >= 0 && u < N) {
-        const int jj = __builtin_popcount(act & ((1u << (u >> 5)) - 1u));   // compacted word
-        atomicOr(&stage[(i / S) * STR + jj], 1u << (u & 31));
+    auto put = [&](int r, int u) __attribute__((always_inline)) {
+      if (u >= 0 && u < N)
+        atomicOr(&stage[r * kStride + __builtin_popcount(act & ((1u << (u >> 5)) - 1u))],
+                 1u << (u & 31));
+    };
+    if ((S & 3) == 0) {          // 16-byte loads, 8 per lane in flight
+      const int n4 = (nrows * S) >> 2;
+      const int4* b4 = reinterpret_cast<const int4*>(base);
+      for (int i0 = 0; i0 < n4; i0 += 64 * 8) {
+        int4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int i = i0 + 64 * j + lane;
+          v[j] = (i < n4) ? b4[i] : make_int4(-1, -1, -1, -1);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = ((i0 + 64 * j + lane) << 2) / S;
+          put(r, v[j].x);
+          put(r, v[j].y);
+          put(r, v[j].z);
+          put(r, v[j].w);
+        }
       }
+    } else {
+      for (int i = lane; i < nrows * S; i += 64) put(i / S, base[i]);
     }
     wave_sync();
 #pragma unroll
-    for (int jj = 0; jj < NWB; ++jj) b[c][jj] = stage[lane * STR + jj];
+    for (int jj = 0; jj < NWB; ++jj) bc[jj] = stage[lane * kStride + jj];
     wave_sync();
-  }
+  };
+  build_chunk(b[0], 0);
+  if constexpr (C > 1) build_chunk(b[1], 1);
+  if constexpr (C > 2) build_chunk(b[2], 2);
+  if constexpr (C > 3) build_chunk(b[3], 3);
 
-  uint32_t U[NWB];
-  uint32_t cost[C];
+  // cost(c) = |B_c \ U| = tot_c - gain_c with gain_c = |B_c & U|, kept
+  // incrementally: a word where U grows by delta adds popcount(B_c & delta)
+  uint32_t tot[C], gain[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    tot[c] = 0;
+#pragma unroll
+    for (int jj = 0; jj < NWB; ++jj) tot[c] += __builtin_popcount(b[c][jj]);
+  }
   uint32_t avail = 0;                      // bit c: candidate 64c + lane unassigned
 #pragma unroll
   for (int c = 0; c < C; ++c)
     if (64 * c + lane < Wr) avail |= 1u << c;
+  uint32_t U[NWB];                         // the group's union (wave-uniform)
+  uint32_t w[NWB];                         // the chosen candidate's words
+
+  // the chosen candidate's words, read from its lane (wave-uniform result)
+  auto fetch = [&](int cb, int lb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+      if (c == cb) {
+#pragma unroll
+        for (int jj = 0; jj < NWB; ++jj) w[jj] = __builtin_amdgcn_readlane(b[c][jj], lb);
+      }
+  };
+  // every candidate gains the pages of delta in word jj
+  auto add_gain = [&](int jj, uint32_t delta) __attribute__((always_inline)) {
+#pragma unroll
+    for (int c = 0; c < C; ++c) gain[c] += __builtin_popcount(b[c][jj] & delta);
+  };
 
   int pos = 0;
   while (pos < Wr) {
@@ -96,44 +147,36 @@ __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, i
     if (lane == lb) avail &= ~(1u << cb);
     if (lane == 0) order[pos] = (int)best;
     ++pos;
+    fetch(cb, lb);
 #pragma unroll
-    for (int c = 0; c < C; ++c)
-      if (c == cb) {
+    for (int c = 0; c < C; ++c) gain[c] = 0;
 #pragma unroll
-        for (int jj = 0; jj < NWB; ++jj) U[jj] = __builtin_amdgcn_readlane(b[c][jj], lb);
-      }
-#pragma unroll
-    for (int c = 0; c < C; ++c) {
-      uint32_t x = 0;
-#pragma unroll
-      for (int jj = 0; jj < NWB; ++jj) x += __builtin_popcount(b[c][jj] & ~U[jj]);
-      cost[c] = x;
+    for (int jj = 0; jj < NWB; ++jj) {
+      U[jj] = w[jj];
+      if (w[jj]) add_gain(jj, w[jj]);
     }
     // ---- joins: the unassigned query adding the fewest new pages
     for (int members = 1; members < g && pos < Wr; ++members) {
       key = kNone;
 #pragma unroll
       for (int c = 0; c < C; ++c)
-        if ((avail >> c) & 1u) key = min(key, (cost[c] << 10) | (uint32_t)(64 * c + lane));
+        if ((avail >> c) & 1u)
+          key = min(key, ((tot[c] - gain[c]) << 10) | (uint32_t)(64 * c + lane));
       best = __builtin_amdgcn_readfirstlane(wave_min_dpp(key) & 1023u);
       cb = best >> 6;
       lb = best & 63;
       if (lane == lb) avail &= ~(1u << cb);
       if (lane == 0) order[pos] = (int)best;
       ++pos;
+      fetch(cb, lb);
 #pragma unroll
-      for (int c = 0; c < C; ++c)
-        if (c == cb) {
-#pragma unroll
-          for (int jj = 0; jj < NWB; ++jj) {
-            const uint32_t d = __builtin_amdgcn_readlane(b[c][jj], lb) & ~U[jj];
-            if (d) {
-              U[jj] |= d;
-#pragma unroll
-              for (int c2 = 0; c2 < C; ++c2) cost[c2] -= __builtin_popcount(b[c2][jj] & d);
-            }
-          }
+      for (int jj = 0; jj < NWB; ++jj) {
+        const uint32_t d = w[jj] & ~U[jj];
+        if (d) {
+          U[jj] |= d;
+          add_gain(jj, d);
         }
+      }
     }
   }
 }
@@ -143,8 +186,8 @@ __global__ __launch_bounds__(64) void group_kernel(const int32_t* __restrict__ s
                                                    int32_t* __restrict__ ids, int T, int S,
                                                    int N, int W, int g, int n_windows) {
   extern __shared__ uint32_t lds[];
-  uint32_t* stage = lds;                                  // [64][33] one candidate chunk
-  int* order = reinterpret_cast<int*>(lds + 64 * 33);     // [C * 64] emission order
+  uint32_t* stage = lds;                                   // [64][kStride] one chunk's bitsets
+  int* order = reinterpret_cast<int*>(lds + 64 * kStride); // [C * 64] emission order
   const int lane = threadIdx.x;
   const int h = blockIdx.x / n_windows;
   const int w0 = (blockIdx.x % n_windows) * W;
@@ -153,9 +196,29 @@ __global__ __launch_bounds__(64) void group_kernel(const int32_t* __restrict__ s
 
   // words (32 pages each) that some candidate of the window uses
   uint32_t act = 0;
-  for (int i = lane; i < Wr * S; i += 64) {
-    const int u = wbase[i];
-    if (u >= 0 && u < N) act |= 1u << (u >> 5);
+  if ((S & 3) == 0) {
+    const int n4 = (Wr * S) >> 2;
+    const int4* w4 = reinterpret_cast<const int4*>(wbase);
+    for (int i0 = 0; i0 < n4; i0 += 64 * 8) {
+      int4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = i0 + 64 * j + lane;
+        v[j] = (i < n4) ? w4[i] : make_int4(-1, -1, -1, -1);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (e[k] >= 0 && e[k] < N) act |= 1u << (e[k] >> 5);
+      }
+    }
+  } else {
+    for (int i = lane; i < Wr * S; i += 64) {
+      const int u = wbase[i];
+      if (u >= 0 && u < N) act |= 1u << (u >> 5);
+    }
   }
   act = wave_or(act);
   const int nact = __builtin_popcount(act);
@@ -173,7 +236,7 @@ template <int C>
 hipError_t launch_c(const pw_shape& s, const int32_t* sel, int W, int g, int32_t* ids,
                     hipStream_t stream) {
   const int n_windows = (s.T + W - 1) / W;
-  const size_t lds = (size_t)64 * 33 * 4 + (size_t)C * 64 * 4;
+  const size_t lds = ((size_t)64 * kStride + (size_t)C * 64) * 4;
   hipLaunchKernelGGL(group_kernel<C>, dim3(s.H_kv * n_windows), dim3(64), lds, stream, sel, ids,
                      s.T, s.S, s.N_pages, W, g, n_windows);
   return hipGetLastError();
