@@ -68,15 +68,17 @@ def kernel_hash() -> str:
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
 
 
-def recorded_traffic(per_launch_key: str):
-    """HBM bytes per launch measured with rocprofv3 counters, if taken on this kernel source."""
+def recorded_traffic():
+    """HBM bytes of one pw_union_attention call (re-tiling + attention kernels), from the
+    rocprofv3 FETCH_SIZE / WRITE_SIZE passes stored under profiles/, each scaled by what the
+    same counter reads for a plain 1 GiB copy; None unless taken on this kernel source."""
     path = os.path.join(ROOT, "profiles", "union_attn_counters.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
     if rec.get("kernel_sha256_16") != kernel_hash():
         return None
-    return rec.get(per_launch_key)
+    return rec.get("hbm_bytes_per_call")
 
 
 def cpu_baseline(inp, wl, seconds: float):
@@ -219,10 +221,11 @@ def main():
     attn_avg_s = float(attn_ms.mean()) * 1e-3
     mfma_tflops = comp_flops / attn_avg_s / 1e12
     gbs = alg_bytes / attn_avg_s / 1e9
-    traffic = recorded_traffic("hbm_bytes_per_launch")
+    traffic = recorded_traffic()
     roof = {"bound": "mfma", "achieved": mfma_tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": mfma_tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic,
-            "kernel": "union_attn_kernel<128,1>", "flops_per_unit": flop_unit,
+            "kernel": "pw_union_attention call (tile_kv_kernel + union_attn_kernel)",
+            "flops_per_unit": flop_unit,
             "units_per_launch": n_units,
             "hbm_definition": {"algorithmic_bytes": alg_bytes, "achieved_GBs": gbs,
                                "peak_GBs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS}}
@@ -274,7 +277,7 @@ def main():
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3/bf16",
         "data": "synthetic (seeded captures, Q/K/V ~ N(0,1), e4m3fn KV with per-page scales)",
         "config": {"workload": wl.name, "tokens": wl.T, "H_q": wl.H_q, "H_kv": wl.H_kv,
                    "head_dim": wl.D, "page": wl.P, "selected_pages": wl.S, "W": wl.W, "g": wl.g,
