@@ -75,11 +75,25 @@ __device__ __forceinline__ int tile_key(int i, int kt) {
   return 32 * ((i >> 2) & 1) + 16 * kt + 4 * (i >> 3) + (i & 3);
 }
 
+// Maxima of scores that come straight from the matrix cores (never a
+// signalling NaN): plain v_max3 / v_max, without the quieting v_max x, x that
+// fmaxf adds per operand in IEEE mode.
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
 // Lanes l and l ^ 32 hold the two key halves of the same query row: combine
 // them with one VALU lane swap (no LDS round trip).
 __device__ __forceinline__ float half_max(float x) {
   const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
+  return max_raw(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
 }
 __device__ __forceinline__ float half_sum(float x) {
   const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -137,7 +151,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, PIPE ? 1 : 2) void union_attn_
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int hf = lane >> 5;      // lane half
   const int col = lane & 31;     // query row within a tile
 
@@ -223,7 +237,8 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, PIPE ? 1 : 2) void union_attn_
   if (m1) list[n_u++] = (uint32_t)(2 * k + 1) | (m1 << 16);
   wave_sync();
   }
-  int tmin = wave_min_u32(my_t >= 0 ? (uint32_t)my_t : 0xFFFFFFFFu);
+  const int tmin = __builtin_amdgcn_readfirstlane(
+      (int)wave_min_u32(my_t >= 0 ? (uint32_t)my_t : 0xFFFFFFFFu));
 
   // ---- per-lane query rows and Q operands (B of S^T = K Q^T).  Each bf16 row
   // is scaled by a power of two (absmax into [128, 256)) and split exactly into
@@ -303,15 +318,17 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, PIPE ? 1 : 2) void union_attn_
   uint4 kbuf[2][2][KCH], vbuf[2][DT][2];
   f32x16 sacc[2][NT][2];
   float ksr[2], vsr[2];
-  auto page_of = [&](int i) { return (int)(list[min(i, n_u - 1)] & 0xFFFF); };
+  auto page_of = [&](int i) {       // wave-uniform
+    return __builtin_amdgcn_readfirstlane((int)(list[min(i, n_u - 1)] & 0xFFFF));
+  };
   const int block_bytes = 64 * D;
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.Kt, (short)0, 0x7FFFFFFF, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.Vt, (short)0, 0x7FFFFFFF, 0x00020000);
   const int loff = 16 * lane;
-  auto block_of = [&](int u) {
-    return (__builtin_amdgcn_readfirstlane(u) * p.Hkv + h) * block_bytes;
+  auto block_of = [&](int u) {     // wave-uniform: a scalar offset, no per-lane address
+    return __builtin_amdgcn_readfirstlane((u * p.Hkv + h) * block_bytes);
   };
   auto load_k = [&](uint4 (&kr)[2][KCH], int u) {
     const int so = block_of(u);
@@ -387,11 +404,10 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, PIPE ? 1 : 2) void union_attn_
     const float ivs = __builtin_amdgcn_rcpf(vs_raw);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      float mx = -INFINITY;
+      float mx = max_raw(sc[nt][0][0], sc[nt][0][1]);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; r += 2) mx = fmaxf(mx, fmaxf(sc[nt][kt][r], sc[nt][kt][r + 1]));
+      for (int i = 2; i < 32; i += 2)
+        mx = max3_raw(mx, sc[nt][i >> 4][i & 15], sc[nt][i >> 4][(i & 15) + 1]);
       mx = half_max(mx);
       const bool member = slot[nt] >= 0 && ((mbits >> slot[nt]) & 1u);
       const float ksc = ksc0 * rscale[nt];
@@ -519,7 +535,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, PIPE ? 1 : 2) void union_attn_
     bf16x8 pB[NT][4];
     float alph[NT];
     for (int up = 0; up < n_u; ++up) {
-      const uint32_t ent = list[up];
+      const uint32_t ent = __builtin_amdgcn_readfirstlane(list[up]);
       const float ks_c = ksr[0], vs_c = vsr[0];
       const int u1 = page_of(up + 1);
       qk(kbuf[0], sacc[0]);
