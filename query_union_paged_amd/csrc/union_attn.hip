@@ -29,9 +29,6 @@
 // once, by its wave.  There are no atomics and no partial outputs.
 #include "pw_internal.h"
 
-#ifndef PW_UA_PIPE
-#define PW_UA_PIPE 0      // 1: software-pipelined schedule at one wave per SIMD
-#endif
 #ifndef PW_UA_WG_WAVES
 #define PW_UA_WG_WAVES 4  // waves (independent groups) per workgroup
 #endif
@@ -141,11 +138,11 @@ __global__ __launch_bounds__(256) void tile_kv_kernel(const uint8_t* __restrict_
 // MODE kUnionMode: groups of query IDs, union of their selected pages, O out.
 // MODE kPairMode: up to 8 entries of one page pair's membership list, the pair's
 // pages they selected, unnormalised partials out (direct KV-page union).
-template <int D, bool P64, bool PIPE, int MODE>
-__global__ __launch_bounds__(64 * PW_UA_WG_WAVES, PIPE ? 1 : 2) void union_attn_kernel(UAParams p) {
+template <int D, int P, int MODE>
+__global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAParams p) {
   constexpr int NT = 1;          // one 32-row tile per wave
-  // P64: pages of exactly 64 keys (no key-range guards); otherwise P in {16, 32}.
-  const int P = P64 ? 64 : p.P;
+  // P in {16, 32, 64} keys per page; the tiled pages always hold 64 key slots
+  // (slots >= P are zero and masked here).
   constexpr int KCH = D / 32;    // uint4 chunks of K per lane per key tile
   constexpr int DT = D / 32;     // output tiles over d (PV)
   extern __shared__ __align__(16) unsigned char smem[];
@@ -315,9 +312,9 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, PIPE ? 1 : 2) void union_attn_
   // K and V come from the tiled copies (tile_kv_kernel): the block of (page u,
   // KV head h) holds 64 key slots x D in MFMA operand order, so every load
   // below is one contiguous 1 KB read of the wave (lane l at 16 * l).
-  uint4 kbuf[2][2][KCH], vbuf[2][DT][2];
-  f32x16 sacc[2][NT][2];
-  float ksr[2], vsr[2];
+  uint4 kbuf[2][KCH], vbuf[DT][2];
+  f32x16 sacc[NT][2];
+  float ksr = 0.f, vsr = 0.f;
   auto page_of = [&](int i) {       // wave-uniform
     return __builtin_amdgcn_readfirstlane((int)(list[min(i, n_u - 1)] & 0xFFFF));
   };
@@ -326,7 +323,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, PIPE ? 1 : 2) void union_attn_
       __builtin_amdgcn_make_buffer_rsrc((void*)p.Kt, (short)0, 0x7FFFFFFF, 0x00020000);
   const __amdgpu_buffer_rsrc_t vrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.Vt, (short)0, 0x7FFFFFFF, 0x00020000);
-  const int loff = 16 * lane;
+  const int loff = 16 * lane;       // the only per-lane part of a page load's address
   auto block_of = [&](int u) {     // wave-uniform: a scalar offset, no per-lane address
     return __builtin_amdgcn_readfirstlane((u * p.Hkv + h) * block_bytes);
   };
@@ -337,7 +334,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, PIPE ? 1 : 2) void union_attn_
 #pragma unroll
       for (int c = 0; c < KCH; ++c)
         kr[kt][c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  krs, loff + 1024 * (kt * KCH + c), so, 0));
+                                                  krs, loff, so + 1024 * (kt * KCH + c), 0));
   };
   auto load_v = [&](uint4 (&vr)[DT][2], int u) {
     const int so = block_of(u);
@@ -346,7 +343,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, PIPE ? 1 : 2) void union_attn_
 #pragma unroll
       for (int j = 0; j < 2; ++j)
         vr[dt][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  vrs, loff + 1024 * (2 * dt + j), so, 0));
+                                                  vrs, loff, so + 1024 * (2 * dt + j), 0));
   };
   const float* kscale = p.scales + h;                       // [N][Hkv]
   const float* vscale = p.scales + (size_t)p.N * p.Hkv + h;
@@ -381,7 +378,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, PIPE ? 1 : 2) void union_attn_
   // ---- stages of one page: mask -> softmax -> (rescale) -> PV
   // causal / page-size mask, only where some key can lie after a member
   auto mask_page = [&](f32x16 (&sc)[NT][2], int u) {
-    const bool need_mask = !P64 || (u * P + P - 1 > tmin);
+    const bool need_mask = P < 64 || (u * P + P - 1 > tmin);
     if (need_mask) {
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
@@ -390,7 +387,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, PIPE ? 1 : 2) void union_attn_
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = 32 * hf + 16 * kt + r;
-            if ((!P64 && key >= P) || u * P + key > trow[nt]) sc[nt][kt][r] = -INFINITY;
+            if (key >= P || u * P + key > trow[nt]) sc[nt][kt][r] = -INFINITY;
           }
     }
   };
@@ -464,92 +461,34 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, PIPE ? 1 : 2) void union_attn_
     }
   };
 
-  if (PIPE) {
-    // Three-stage software pipeline, one wave per SIMD.  Iteration u runs
-    // PV(u-1), softmax(u) and QK(u+1) in one basic block (independent work for
-    // the matrix cores and the VALU), after the rarely taken rescale and mask
-    // branches.  K is fetched 2 pages ahead, V one page ahead of its use.
-    // K(x), V(x), S(x), P(x) live in buffer x & 1.
-    bf16x8 pbuf[2][NT][4];
-    float alph[NT];
-    if (n_u > 0) {
-      load_k(kbuf[0], page_of(0));
-      load_k(kbuf[1], page_of(1));
-      load_v(vbuf[0], page_of(0));
-      load_v(vbuf[1], page_of(1));
-      ksr[0] = kscale[(size_t)page_of(0) * p.Hkv];
-      vsr[0] = vscale[(size_t)page_of(0) * p.Hkv];
-      ksr[1] = kscale[(size_t)page_of(1) * p.Hkv];
-      vsr[1] = vscale[(size_t)page_of(1) * p.Hkv];
-      qk(kbuf[0], sacc[0]);
-      load_k(kbuf[0], page_of(2));
-      // iteration 0: no PV yet
-      const uint32_t ent = list[0];
-      mask_page(sacc[0], ent & 0xFFFF);
-      softmax(sacc[0], ent >> 16, ksr[0], vsr[0], pbuf[0], alph);
-      ksr[0] = kscale[(size_t)page_of(2) * p.Hkv];
-      vsr[0] = vscale[(size_t)page_of(2) * p.Hkv];
-      qk(kbuf[1], sacc[1]);
-      load_k(kbuf[1], page_of(3));
-    }
-    for (int u0 = 1; u0 < n_u + 1; u0 += 2) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {      // page u has parity c ^ 1 (u0 is odd)
-        const int u = u0 + c;
-        const int pc = c ^ 1, pp = c;    // buffers of page u and page u - 1
-        if (u < n_u) {
-          rescale(alph);
-          const uint32_t ent = list[u];
-          mask_page(sacc[pc], ent & 0xFFFF);
-          const float ks_c = ksr[pc], vs_c = vsr[pc];
-          pv(vbuf[pp], pbuf[pp]);
-          softmax(sacc[pc], ent >> 16, ks_c, vs_c, pbuf[pc], alph);
-          qk(kbuf[pp], sacc[pp]);        // page u + 1 (past the end: recomputes the last page)
-          if (PIPE) {
-#pragma unroll
-            for (int i = 0; i < 24; ++i) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
-            }
-          }
-          load_v(vbuf[pp], page_of(u + 1));
-          load_k(kbuf[pp], page_of(u + 3));
-          ksr[pc] = kscale[(size_t)page_of(u + 2) * p.Hkv];
-          vsr[pc] = vscale[(size_t)page_of(u + 2) * p.Hkv];
-        } else if (u == n_u) {
-          rescale(alph);
-          pv(vbuf[pp], pbuf[pp]);        // the last page's PV
-        }
-      }
-    }
-  } else {
-    // Plain order with one page of K/V ahead, two waves per SIMD overlapping
-    // each other's matrix and vector work.
-    if (n_u > 0) {
-      const int u0 = page_of(0);
-      load_k(kbuf[0], u0);
-      load_v(vbuf[0], u0);
-      ksr[0] = kscale[(size_t)u0 * p.Hkv];
-      vsr[0] = vscale[(size_t)u0 * p.Hkv];
-    }
-    bf16x8 pB[NT][4];
-    float alph[NT];
-    for (int up = 0; up < n_u; ++up) {
-      const uint32_t ent = __builtin_amdgcn_readfirstlane(list[up]);
-      const float ks_c = ksr[0], vs_c = vsr[0];
-      const int u1 = page_of(up + 1);
-      qk(kbuf[0], sacc[0]);
-      __builtin_amdgcn_sched_barrier(0);    // K registers are free after the MFMAs read them
-      load_k(kbuf[0], u1);
-      ksr[0] = kscale[(size_t)u1 * p.Hkv];
-      vsr[0] = vscale[(size_t)u1 * p.Hkv];
-      mask_page(sacc[0], ent & 0xFFFF);
-      softmax(sacc[0], ent >> 16, ks_c, vs_c, pB, alph);
-      rescale(alph);
-      pv(vbuf[0], pB);
-      __builtin_amdgcn_sched_barrier(0);
-      load_v(vbuf[0], u1);
-    }
+  // One page of K/V ahead, two waves per SIMD overlapping each other's matrix
+  // and vector work.  (Software-pipelined schedules that keep the next page's
+  // scores in flight during the softmax need more than the 256 registers a
+  // wave has at this occupancy; they spilled and ran slower.)
+  if (n_u > 0) {
+    const int u0 = page_of(0);
+    load_k(kbuf, u0);
+    load_v(vbuf, u0);
+    ksr = kscale[(size_t)u0 * p.Hkv];
+    vsr = vscale[(size_t)u0 * p.Hkv];
+  }
+  bf16x8 pB[NT][4];
+  float alph[NT];
+  for (int up = 0; up < n_u; ++up) {
+    const uint32_t ent = __builtin_amdgcn_readfirstlane(list[up]);
+    const float ks_c = ksr, vs_c = vsr;
+    const int u1 = page_of(up + 1);
+    qk(kbuf, sacc);
+    __builtin_amdgcn_sched_barrier(0);    // K registers are free after the MFMAs read them
+    load_k(kbuf, u1);
+    ksr = kscale[(size_t)u1 * p.Hkv];
+    vsr = vscale[(size_t)u1 * p.Hkv];
+    mask_page(sacc, ent & 0xFFFF);
+    softmax(sacc, ent >> 16, ks_c, vs_c, pB, alph);
+    rescale(alph);
+    pv(vbuf, pB);
+    __builtin_amdgcn_sched_barrier(0);
+    load_v(vbuf, u1);
   }
 
   if constexpr (MODE == kPairMode) {
@@ -595,13 +534,13 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, PIPE ? 1 : 2) void union_attn_
 
 template <int D, int MODE>
 hipError_t launch_d(const UAParams& prm, int blocks, size_t lds, hipStream_t stream) {
-  constexpr bool pipe = PW_UA_PIPE != 0;
+  const dim3 grid(blocks), block(64 * PW_UA_WG_WAVES);
   if (prm.P == 64)
-    hipLaunchKernelGGL((union_attn_kernel<D, true, pipe, MODE>), dim3(blocks),
-                       dim3(64 * PW_UA_WG_WAVES), lds, stream, prm);
+    hipLaunchKernelGGL((union_attn_kernel<D, 64, MODE>), grid, block, lds, stream, prm);
+  else if (prm.P == 32)
+    hipLaunchKernelGGL((union_attn_kernel<D, 32, MODE>), grid, block, lds, stream, prm);
   else
-    hipLaunchKernelGGL((union_attn_kernel<D, false, pipe, MODE>), dim3(blocks),
-                       dim3(64 * PW_UA_WG_WAVES), lds, stream, prm);
+    hipLaunchKernelGGL((union_attn_kernel<D, 16, MODE>), grid, block, lds, stream, prm);
   return hipGetLastError();
 }
 
