@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--cold", type=int, default=5, help="cold-cache runs (MALL/L2 flushed)")
     ap.add_argument("--gen-workers", type=int, default=16,
                     help="processes for input generation (0: in-process, e.g. under a profiler)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the complete call over W in {32..256} x g in {4, 8, 16} "
+                         "(regrouped, and identity grouping at each g)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="after the timed region, one plain 1 GiB device-to-device copy "
                          "(reference dispatch for scaling HBM byte counters)")
@@ -127,7 +130,60 @@ def cpu_baseline(inp, wl, seconds: float):
                   f"fp64 numpy, {dt:.1f} s; full-job estimate {dt * wl.T / n:.0f} s",
         "greedy_windows_per_s": nwin * wl.H_kv / gdt,
         "greedy_full_estimate_s": gdt * (wl.T // wl.W) / nwin,
+        "cpu_model": cpu_model(),
     }
+
+
+def sweep(pw, torch, wl, inp, dev, shp, O, ws, reps: int = 5):
+    """Complete-call cost over the window W and group size g (regrouped and identity)."""
+    stream = torch.cuda.current_stream()
+    ident = torch.arange(wl.T, dtype=torch.int32, device="cuda").repeat(wl.H_kv, 1).contiguous()
+    ids = torch.empty_like(ident)
+
+    def timed(fn):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def attn(g, idv):
+        return lambda: pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"],
+                                             dev["scales"], dev["sel_pages"], idv, g, O=O,
+                                             workspace=ws)
+    rows = []
+    for g in (4, 8, 16):
+        if g * wl.G > 64 or g * wl.S > 1024:
+            continue
+        a_id = timed(attn(g, ident))
+        u_id = union_stats(inp["sel_pages"], ident.cpu().numpy(), g, wl.N)
+        rows.append({"W": None, "g": g, "grouping": "identity", "search_ms": 0.0,
+                     "attention_ms": a_id, "call_ms": a_id, "union_pages_mean": float(u_id.mean())})
+        for W in (32, 64, 128, 256):
+            if W < g:
+                continue
+            s_ms = timed(lambda: pw.pw_group(shp, dev["sel_pages"], W, g, query_ids=ids))
+            a_ms = timed(attn(g, ids))
+            u = union_stats(inp["sel_pages"], ids.cpu().numpy(), g, wl.N)
+            rows.append({"W": W, "g": g, "grouping": "regrouped", "search_ms": s_ms,
+                         "attention_ms": a_ms, "call_ms": s_ms + a_ms,
+                         "union_pages_mean": float(u.mean()), "vs_identity": a_id / (s_ms + a_ms)})
+            log(f"[sweep] {wl.name} W={W} g={g}: search {s_ms:.3f} ms, attention {a_ms:.3f} ms, "
+                f"union {u.mean():.1f} pages, identity {a_id:.3f} ms")
+    return rows
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def main():
@@ -253,20 +309,22 @@ def main():
                           "union_pages_mean": float(us.mean()), "union_pages_total": int(us.sum())}
         arms["regroup_gain_vs_identity"] = arms["identity_union8"]["ms"] / ms_per_step
         # the direct KV-page union (design-study comparison)
-        ws = torch.empty(pw.pw_dense_union_ref_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
+        dws = torch.empty(pw.pw_dense_union_ref_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
         pw.pw_dense_union_ref(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
-                              dev["sel_pages"], O=O, workspace=ws)
+                              dev["sel_pages"], O=O, workspace=dws)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         for _ in range(2):
             pw.pw_dense_union_ref(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
-                                  dev["sel_pages"], O=O, workspace=ws)
+                                  dev["sel_pages"], O=O, workspace=dws)
         b.record(stream)
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / 2
         arms["direct_page_union"] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12,
-                                     "workspace_GiB": ws.numel() / 2 ** 30}
-        del ws
+                                     "workspace_GiB": dws.numel() / 2 ** 30}
+        del dws
+
+    swp = sweep(pw, torch, wl, inp, dev, shp, O, ws) if args.sweep else None
 
     cpu = None
     if not args.no_cpu:
@@ -291,6 +349,7 @@ def main():
         "union": {"pages_mean": float(usz.mean()), "pages_max": int(usz.max()),
                   "efficiency_useful_over_computed": F_u / comp_flops},
         "roofline": roof, "arms": arms, "cpu_baseline": cpu,
+        **({"sweep": swp} if swp is not None else {}),
     }
     print(json.dumps(out), flush=True)
 

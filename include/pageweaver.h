@@ -105,7 +105,7 @@ typedef struct pw_shape {
  * written window by window, group by group, members in insertion order.  The
  * result is unique, so it is bit-exact against any correct implementation.
  *
- * In : sel_pages (see layouts), W in [1, 256], g in [1, 8].
+ * In : sel_pages (see layouts), W in [1, 256], g in [1, 16].
  * Out: query_ids int32 [H_kv][T] (every entry written).
  * Support set: N_pages <= 1024.  Workspace: none (returns 0).
  * ------------------------------------------------------------------------- */
@@ -133,7 +133,7 @@ pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W,
  * The result of a row does not depend on which other queries share its group.
  *
  * In : Q, K_fp8, V_fp8, scales, sel_pages, query_ids (see layouts), g in
- *      [1, 8] with g * G <= 64.  IDs outside [0, T) are skipped; a
+ *      [1, 16] with g * G <= 64 and g * S <= 1024.  IDs outside [0, T) are skipped; a
  *      query_ids row that is not a permutation leaves unlisted rows of O
  *      unwritten.
  * Out: O.

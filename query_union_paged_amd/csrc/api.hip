@@ -44,7 +44,7 @@ pw_status check_shape(const pw_shape* s) {
 
 pw_status check_attention_support(const pw_shape* s, int g) {
   const int G = s->H_q / s->H_kv;
-  if (g < 1 || g > 8) return fail(PW_ERR_UNSUPPORTED, "g = %d outside [1, 8]", g);
+  if (g < 1 || g > 16) return fail(PW_ERR_UNSUPPORTED, "g = %d outside [1, 16]", g);
   if (g * G > 64) return fail(PW_ERR_UNSUPPORTED, "g * G = %d exceeds 64 query rows", g * G);
   if (s->D != 64 && s->D != 128) return fail(PW_ERR_UNSUPPORTED, "D = %d not in {64, 128}", s->D);
   if (s->P != 16 && s->P != 32 && s->P != 64)
@@ -84,7 +84,7 @@ pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W, i
   if (st != PW_OK) return st;
   if (!sel_pages || !query_ids) return fail(PW_ERR_NULL, "sel_pages and query_ids are required");
   if (W < 1 || W > 256) return fail(PW_ERR_UNSUPPORTED, "W = %d outside [1, 256]", W);
-  if (g < 1 || g > 8) return fail(PW_ERR_UNSUPPORTED, "g = %d outside [1, 8]", g);
+  if (g < 1 || g > 16) return fail(PW_ERR_UNSUPPORTED, "g = %d outside [1, 16]", g);
   if (shape->N_pages > 1024)
     return fail(PW_ERR_UNSUPPORTED, "N_pages = %d exceeds 1024 for the search", shape->N_pages);
   return hip_status(pw::launch_group(*shape, sel_pages, W, g, query_ids, (hipStream_t)stream),

@@ -173,13 +173,13 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   const int g0 = (gid - h * p.groups_per_head) * p.g;
   gm = min(p.g, p.T - g0);
   uint32_t* mask32 = reinterpret_cast<uint32_t*>(wbase + (size_t)p.n_umax * 4);
-  const int n_mwords = (p.N + 3) >> 2;
+  const int n_mwords = (p.N + 1) >> 1;
   if (lane < gm) {
     const int t = p.ids[(size_t)h * p.T + g0 + lane];
     my_t = (t >= 0 && t < p.T) ? t : -1;
   }
 
-  // ---- union + membership: mask byte per page, bit i = member i selected it
+  // ---- union + membership: 16-bit mask per page, bit i = member i selected it
   for (int i = lane; i < n_mwords; i += 64) mask32[i] = 0;
   wave_sync();
   {
@@ -199,14 +199,14 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
     for (int it = 0; it < MAXIT; ++it) {
       if (pg[it] >= 0) {
         const int u = pg[it] & 0xFFFF, i = pg[it] >> 16;
-        atomicOr(&mask32[u >> 2], (1u << i) << ((u & 3) * 8));
+        atomicOr(&mask32[u >> 1], (1u << i) << ((u & 1) * 16));
       }
     }
   }
   wave_sync();
   for (int c0 = 0; c0 < p.N; c0 += 64) {
     const int u = c0 + lane;
-    const uint32_t m = (u < p.N) ? ((mask32[u >> 2] >> ((u & 3) * 8)) & 0xFFu) : 0u;
+    const uint32_t m = (u < p.N) ? ((mask32[u >> 1] >> ((u & 1) * 16)) & 0xFFFFu) : 0u;
     const uint64_t bal = __ballot(m != 0);
     if (m) list[n_u + lane_prefix(bal)] = (uint32_t)u | (m << 16);
     n_u += __popcll(bal);
@@ -584,7 +584,7 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
   prm.groups_per_head = (s.T + g - 1) / g;
   prm.total_groups = prm.groups_per_head * s.H_kv;
   prm.n_umax = (g * s.S < s.N_pages) ? g * s.S : s.N_pages;
-  const int mask_bytes = ((s.N_pages + 3) / 4) * 4;
+  const int mask_bytes = ((s.N_pages + 1) / 2) * 4;
   prm.lds_wave = ((prm.n_umax * 4 + mask_bytes) + 15) / 16 * 16;
   prm.n_rt = (g * prm.G + 31) / 32;
   prm.total_items = prm.total_groups * prm.n_rt;

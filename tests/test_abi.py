@@ -55,7 +55,7 @@ def test_group_validation():
     assert _group(_shape(), ids=None) == pw.PW_ERR_NULL
     assert _group(_shape(), W=0) == pw.PW_ERR_UNSUPPORTED
     assert _group(_shape(), W=257) == pw.PW_ERR_UNSUPPORTED
-    assert _group(_shape(), g=9) == pw.PW_ERR_UNSUPPORTED
+    assert _group(_shape(), g=17) == pw.PW_ERR_UNSUPPORTED
     assert _group(_shape(T=2048 * 16, N_pages=2048)) == pw.PW_ERR_UNSUPPORTED
     assert b"W = 257" in (_group(_shape(), W=257) and pw._lib.pw_last_error())
     assert pw._lib.pw_group_workspace_bytes(ctypes.byref(_shape()), 32, 8) == 0
@@ -67,6 +67,8 @@ def test_attention_validation():
     assert _attn(_shape(D=96)) == pw.PW_ERR_UNSUPPORTED
     assert _attn(_shape(P=8, N_pages=128)) == pw.PW_ERR_UNSUPPORTED
     assert _attn(_shape(), g=0) == pw.PW_ERR_UNSUPPORTED
+    assert _attn(_shape(), g=17) == pw.PW_ERR_UNSUPPORTED
+    assert _attn(_shape(H_q=8, H_kv=1), g=16) == pw.PW_ERR_UNSUPPORTED     # 128 query rows
     assert _attn(_shape(H_q=16, H_kv=1), g=8) == pw.PW_ERR_UNSUPPORTED   # 128 query rows
     assert _attn(_shape(S=200), g=8) == pw.PW_ERR_UNSUPPORTED           # g * S > 1024
     assert _attn(_shape(N_pages=65536, T=65536 * 16)) == pw.PW_ERR_UNSUPPORTED

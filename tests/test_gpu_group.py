@@ -40,7 +40,8 @@ def test_group_ids_bit_exact(name):
     assert np.array_equal(got, ref), f"{(got != ref).sum()} IDs differ"
 
 
-@pytest.mark.parametrize("W,g", [(32, 1), (32, 3), (64, 8), (96, 8), (128, 4), (256, 8), (200, 5), (256, 2)])
+@pytest.mark.parametrize("W,g", [(32, 1), (32, 3), (64, 8), (96, 8), (128, 4), (256, 8), (200, 5), (256, 2),
+                                 (64, 16), (256, 16), (40, 16)])
 def test_group_windows_and_sizes(W, g):
     # random supports over N = 256 pages, including ragged last windows and groups
     log(f"[case] pw_group random W={W} g={g}")

@@ -84,7 +84,8 @@ def test_8k_peaked_sampled():
 @pytest.mark.parametrize("D,P,Hq,Hkv,S,g", [
     (64, 16, 4, 1, 8, 8), (64, 32, 8, 2, 5, 8), (128, 64, 8, 1, 4, 8),   # G = 8: two row tiles
     (128, 16, 2, 2, 6, 8), (64, 64, 16, 2, 3, 4), (128, 32, 4, 2, 7, 3),  # g = 3: ragged last group
-    (128, 64, 1, 1, 5, 8), (64, 16, 8, 4, 9, 5), (128, 64, 32, 1, 3, 2)])
+    (128, 64, 1, 1, 5, 8), (64, 16, 8, 4, 9, 5), (128, 64, 32, 1, 3, 2),
+    (128, 64, 4, 1, 6, 16), (64, 16, 8, 2, 9, 16), (128, 32, 2, 2, 5, 13)])   # g up to 16
 def test_shapes_and_group_sizes(D, P, Hq, Hkv, S, g):
     log(f"[case] union shape D={D} P={P} Hq={Hq} Hkv={Hkv} S={S} g={g}")
     T = 16 * P
@@ -142,7 +143,7 @@ def test_invalid_arguments_raise():
     ids = torch.arange(64, dtype=torch.int32, device="cuda")[None].contiguous()
     with pytest.raises(pw.PWError) as e:
         pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
-                              dev["sel_pages"], ids, 9)
+                              dev["sel_pages"], ids, 17)
     assert e.value.status == pw.PW_ERR_UNSUPPORTED
     bad = pw.shape(64, 4, 1, 64, 16, 5, 2)
     with pytest.raises((pw.PWError, ValueError)):

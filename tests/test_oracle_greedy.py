@@ -56,7 +56,7 @@ def test_matches_brute_force(seed):
     rng = np.random.default_rng(seed)
     N = int(rng.integers(2, 65))
     W = int(rng.choice([4, 8, 16, 32]))
-    g = int(rng.choice([1, 2, 3, 4, 8]))
+    g = int(rng.choice([1, 2, 3, 4, 8, 16]))
     T = int(W * rng.integers(1, 4) - rng.integers(0, 3))
     S = int(rng.integers(1, 10))
     sel = rng.integers(-2, N + 2, size=(T, S)).astype(np.int32)
