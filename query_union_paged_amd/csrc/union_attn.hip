@@ -172,20 +172,25 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   h = gid / p.groups_per_head;
   const int g0 = (gid - h * p.groups_per_head) * p.g;
   gm = min(p.g, p.T - g0);
-  uint32_t* mask32 = reinterpret_cast<uint32_t*>(wbase + (size_t)p.n_umax * 4);
-  const int n_mwords = (p.N + 1) >> 1;
+  const int nw = (p.N + 31) >> 5;              // words of the page bitset
+  uint32_t* bits = reinterpret_cast<uint32_t*>(wbase + (size_t)p.n_umax * 4);
+  int* prefix = reinterpret_cast<int*>(bits + nw);  // union pages before each word
   if (lane < gm) {
     const int t = p.ids[(size_t)h * p.T + g0 + lane];
     my_t = (t >= 0 && t < p.T) ? t : -1;
   }
 
-  // ---- union + membership: 16-bit mask per page, bit i = member i selected it
-  for (int i = lane; i < n_mwords; i += 64) mask32[i] = 0;
+  // ---- union + membership.  A page bitset marks the union; a scan of its words
+  // gives the ascending page list and, per word, the list position of its first
+  // page; then each (page, member) entry ORs its member bit into the upper half
+  // of that page's list entry.  LDS use is N/4 bytes + 4 per list entry, so N
+  // up to the supported maximum fits.
+  for (int i = lane; i < nw; i += 64) bits[i] = 0;
   wave_sync();
+  constexpr int MAXIT = 16;          // g * S <= 1024 entries
+  int pg[MAXIT];
   {
-    constexpr int MAXIT = 16;        // g * S <= 1024 entries
     const int n_ent = gm * p.S;
-    int pg[MAXIT];
 #pragma unroll
     for (int it = 0; it < MAXIT; ++it) {
       const int e = lane + 64 * it;
@@ -196,20 +201,36 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
       pg[it] = (pg[it] >= 0 && pg[it] < p.N) ? (pg[it] | (i << 16)) : -1;
     }
 #pragma unroll
-    for (int it = 0; it < MAXIT; ++it) {
-      if (pg[it] >= 0) {
-        const int u = pg[it] & 0xFFFF, i = pg[it] >> 16;
-        atomicOr(&mask32[u >> 1], (1u << i) << ((u & 1) * 16));
-      }
-    }
+    for (int it = 0; it < MAXIT; ++it)
+      if (pg[it] >= 0) atomicOr(&bits[(pg[it] & 0xFFFF) >> 5], 1u << (pg[it] & 31));
   }
   wave_sync();
-  for (int c0 = 0; c0 < p.N; c0 += 64) {
-    const int u = c0 + lane;
-    const uint32_t m = (u < p.N) ? ((mask32[u >> 1] >> ((u & 1) * 16)) & 0xFFFFu) : 0u;
-    const uint64_t bal = __ballot(m != 0);
-    if (m) list[n_u + lane_prefix(bal)] = (uint32_t)u | (m << 16);
-    n_u += __popcll(bal);
+  for (int c0 = 0; c0 < nw; c0 += 64) {
+    const int w = c0 + lane;
+    uint32_t x = (w < nw) ? bits[w] : 0u;
+    const int cnt = __builtin_popcount(x);
+    int incl = cnt;                    // inclusive scan of the word counts over the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    int pos = n_u + incl - cnt;
+    if (w < nw) prefix[w] = pos;
+    while (x) {
+      list[pos++] = (uint32_t)(32 * w + __builtin_ctz(x));
+      x &= x - 1u;
+    }
+    n_u += __shfl(incl, 63);
+  }
+  wave_sync();
+#pragma unroll
+  for (int it = 0; it < MAXIT; ++it) {
+    if (pg[it] >= 0) {
+      const int u = pg[it] & 0xFFFF, i = pg[it] >> 16;
+      const int r = prefix[u >> 5] + __builtin_popcount(bits[u >> 5] & ((1u << (u & 31)) - 1u));
+      atomicOr(&list[r], (1u << i) << 16);
+    }
   }
   wave_sync();
   } else {
@@ -584,8 +605,8 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
   prm.groups_per_head = (s.T + g - 1) / g;
   prm.total_groups = prm.groups_per_head * s.H_kv;
   prm.n_umax = (g * s.S < s.N_pages) ? g * s.S : s.N_pages;
-  const int mask_bytes = ((s.N_pages + 1) / 2) * 4;
-  prm.lds_wave = ((prm.n_umax * 4 + mask_bytes) + 15) / 16 * 16;
+  const int nw = (s.N_pages + 31) / 32;           // page bitset words, then their list offsets
+  prm.lds_wave = ((prm.n_umax * 4 + 2 * nw * 4) + 15) / 16 * 16;
   prm.n_rt = (g * prm.G + 31) / 32;
   prm.total_items = prm.total_groups * prm.n_rt;
   const int blocks = (prm.total_items + PW_UA_WG_WAVES - 1) / PW_UA_WG_WAVES;

@@ -72,6 +72,7 @@ def test_attention_validation():
     assert _attn(_shape(H_q=16, H_kv=1), g=8) == pw.PW_ERR_UNSUPPORTED   # 128 query rows
     assert _attn(_shape(S=200), g=8) == pw.PW_ERR_UNSUPPORTED           # g * S > 1024
     assert _attn(_shape(N_pages=65536, T=65536 * 16)) == pw.PW_ERR_UNSUPPORTED
+    assert _attn(_shape(N_pages=32769, T=32769 * 16)) == pw.PW_ERR_UNSUPPORTED
     assert _attn(_shape(S=-1)) == pw.PW_ERR_DIMS
     shp = _shape()
     need = pw._lib.pw_union_attention_workspace_bytes(ctypes.byref(shp), 8)

@@ -149,3 +149,33 @@ def test_invalid_arguments_raise():
     with pytest.raises((pw.PWError, ValueError)):
         pw.pw_union_attention(bad, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
                               dev["sel_pages"], ids, 8)
+
+
+def test_largest_page_count():
+    # N_pages = 32768 (the supported maximum) at P = 16: T = 524288 queries, identity groups;
+    # page offsets reach the top of the 32-bit range of the tiled copy
+    T, P, Hq, Hkv, D, S, g = 524288, 16, 4, 1, 64, 4, 8
+    N = T // P
+    log(f"[case] union largest N={N} T={T}")
+    rng = np.random.default_rng(5)
+    gen = torch.Generator().manual_seed(5)
+    t = np.arange(T)
+    own = t // P
+    sel = np.stack([np.zeros(T, np.int64), own, own - 1, (rng.random(T) * (own + 1)).astype(np.int64)],
+                   axis=1)
+    sel = np.where(sel < 0, -1, sel).astype(np.int32)[None]            # [1][T][4], repeats allowed
+    inp = {
+        "q_bits": torch.randn((T, Hq, D), generator=gen).to(torch.bfloat16)
+                       .view(torch.int16).numpy().view(np.uint16),
+        "k_codes": torch.randn((N, Hkv, P, D), generator=gen).to(torch.float8_e4m3fn)
+                        .view(torch.uint8).numpy(),
+        "v_codes": torch.randn((N, Hkv, D, P), generator=gen).to(torch.float8_e4m3fn)
+                        .view(torch.uint8).numpy(),
+        "scales": rng.uniform(0.05, 1.0, size=(2, N, Hkv)).astype(np.float32),
+        "sel_pages": sel,
+    }
+    O, _ = _run(inp, g, "identity")
+    pick = np.concatenate([np.arange(64), np.arange(T - 64, T),
+                           rng.choice(T, size=128, replace=False)])
+    pairs = sorted({(0, int(x)) for x in pick})
+    assert_close(gpu_rows(O, pairs, Hq), oracle_rows(inp, pairs), "largest N")
