@@ -26,7 +26,8 @@ constexpr int kStride = 33;   // LDS words per candidate bitset (32 + 1 pad: con
 
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_min(uint32_t v) {
-  const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+  // every lane has a source lane for these permutes, so the move folds into v_min_u32_dpp
+  const uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
   return min(v, o);
 }
 
@@ -42,10 +43,10 @@ __device__ __forceinline__ uint32_t wave_min_dpp(uint32_t v) {
 }
 
 __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-  v |= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false);
-  v |= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false);
-  v |= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false);
-  v |= (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false);
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true);
+  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true);
   return __builtin_amdgcn_readlane(v, 0) | __builtin_amdgcn_readlane(v, 16) |
          __builtin_amdgcn_readlane(v, 32) | __builtin_amdgcn_readlane(v, 48);
 }

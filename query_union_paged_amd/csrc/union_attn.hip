@@ -6,22 +6,27 @@
 // query IDs without materialising a reordered Q tensor or cross-page partial
 // outputs.
 //
-// Mapping on CDNA4.  One wave owns one 32-row tile of one group (g query IDs
-// of one KV head, M = g*G query rows <= 64, so one or two waves per group) and
-// walks the group's union of pages in ascending page order; four waves share a
-// workgroup only for scheduling.  Per page (64 keys):
-//   S^T = K_page * Q^T     v_mfma_f32_32x32x16_bf16, keys are the MFMA rows
-//                          and query rows the columns, so each lane holds one
-//                          query row (lane & 31) and 32 of its 64 keys;
-//   online softmax         fp32 in registers, row max/sum finished with one
-//                          cross-half exchange (lane ^ 32);
-//   O^T += V_page^T * P^T  v_mfma_f32_32x32x16_bf16, d is the MFMA row.
-// The e4m3fn codes go straight from global memory into MFMA operand registers
-// (each byte is used by exactly one wave once, so LDS staging would only add
-// traffic) and are converted to bf16 exactly; the per-page scales are folded
-// into the scores (k) and into the exponent (v).  The key order inside the
-// 32-row K tiles is permuted so that the PV operands of every lane are 32
-// contiguous tokens of a dim-major V page.
+// Mapping on CDNA4.  A pre-pass (tile_kv_kernel) rewrites the FP8 K and V
+// pages of the call into MFMA operand order, 64 key slots per page.  One wave
+// then owns one 32-row tile of one group (g query IDs of one KV head, M = g*G
+// query rows <= 64, so one or two waves per group) and walks the group's union
+// of pages in ascending page order; four waves share a workgroup only for
+// scheduling.  Per page (64 keys):
+//   S^T = K_page * Q^T     v_mfma_scale_f32_32x32x64_f8f6f4 on the e4m3 codes
+//                          and an exact two-part e4m3 split of each bf16 Q
+//                          row (hi + lo); keys are the MFMA rows and query rows
+//                          the columns, so each lane holds one query row
+//                          (lane & 31) and 32 of its 64 keys;
+//   online softmax         fp32 in registers, log2 domain, lazy rescale; row
+//                          max/sum finished with one cross-half lane swap;
+//   O^T += V_page^T * P^T  v_mfma_f32_32x32x16_bf16 with the V codes converted
+//                          to bf16 exactly; d is the MFMA row.
+// Page loads are contiguous 1 KB wave reads of the tiled copy straight into
+// operand registers (within a group each byte is used by one wave once, so LDS
+// staging would only add traffic); the per-page scales are folded into the
+// scores (k) and into the exponent (v).  The key order inside the 32-row K
+// tiles is permuted so that the PV operands of every lane are 32 contiguous
+// tokens of a dim-major V page.
 //
 // Ownership.  A row whose query did not select a page gets p = 0 and its
 // running max untouched on that page (alpha = 1 exactly), so its result is

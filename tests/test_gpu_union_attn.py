@@ -85,7 +85,8 @@ def test_8k_peaked_sampled():
     (64, 16, 4, 1, 8, 8), (64, 32, 8, 2, 5, 8), (128, 64, 8, 1, 4, 8),   # G = 8: two row tiles
     (128, 16, 2, 2, 6, 8), (64, 64, 16, 2, 3, 4), (128, 32, 4, 2, 7, 3),  # g = 3: ragged last group
     (128, 64, 1, 1, 5, 8), (64, 16, 8, 4, 9, 5), (128, 64, 32, 1, 3, 2),
-    (128, 64, 4, 1, 6, 16), (64, 16, 8, 2, 9, 16), (128, 32, 2, 2, 5, 13)])   # g up to 16
+    (128, 64, 4, 1, 6, 16), (64, 16, 8, 2, 9, 16), (128, 32, 2, 2, 5, 13),   # g up to 16
+    (128, 16, 4, 1, 64, 16)])                                               # g * S = 1024
 def test_shapes_and_group_sizes(D, P, Hq, Hkv, S, g):
     log(f"[case] union shape D={D} P={P} Hq={Hq} Hkv={Hkv} S={S} g={g}")
     T = 16 * P
