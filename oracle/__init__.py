@@ -23,6 +23,9 @@ Modules:
 * ``greedy``     the bounded-window greedy grouping on Python-int bitsets.
 * ``dense_union`` the direct KV-page union (disjoint page pairs, partial
                  outputs merged by log-sum-exp), in fp64.
+* ``selector``   a synthetic dynamic page selector (sink + local pages + top
+                 pages by block key sums), exact/fp64; our own stand-in for the
+                 selection the pages take as given.
 
 Parity status: every function here is pinned by ``tests/test_oracle_*.py``
 against something other than itself (library routines, closed forms, a
