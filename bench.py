@@ -176,6 +176,44 @@ def sweep(pw, torch, wl, inp, dev, shp, O, ws, reps: int = 5):
     return rows
 
 
+def selector_arm(pw, torch, wl, dev, shp, O, ws, reps: int = 5):
+    """The synthetic GPU selector (sink + 2 local pages + top pages by block key sums) and the
+    complete call on its selections, regrouped and with identity grouping."""
+    stream = torch.cuda.current_stream()
+    sws = torch.empty(pw.pw_select_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
+    sel = torch.empty_like(dev["sel_pages"])
+    ids = torch.empty((wl.H_kv, wl.T), dtype=torch.int32, device="cuda")
+    ident = torch.arange(wl.T, dtype=torch.int32, device="cuda").repeat(wl.H_kv, 1).contiguous()
+
+    def timed(fn):
+        fn()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    def attn(idv):
+        return lambda: pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"],
+                                             dev["scales"], sel, idv, wl.g, O=O, workspace=ws)
+    sel_ms = timed(lambda: pw.pw_select(shp, dev["q_bits"], dev["k_codes"], dev["scales"], 2,
+                                        sel_pages=sel, workspace=sws))
+    search_ms = timed(lambda: pw.pw_group(shp, sel, wl.W, wl.g, query_ids=ids))
+    attn_ms = timed(attn(ids))
+    ident_ms = timed(attn(ident))
+    sel_np = sel.cpu().numpy()
+    u = union_stats(sel_np, ids.cpu().numpy(), wl.g, wl.N)
+    ui = union_stats(sel_np, ident.cpu().numpy(), wl.g, wl.N)
+    del sws
+    return {"select_ms": sel_ms, "search_ms": search_ms, "attention_ms": attn_ms,
+            "call_ms": search_ms + attn_ms, "identity_attention_ms": ident_ms,
+            "regroup_gain_vs_identity": ident_ms / (search_ms + attn_ms),
+            "union_pages_mean": float(u.mean()), "identity_union_pages_mean": float(ui.mean()),
+            "n_local": 2}
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -323,6 +361,7 @@ def main():
         arms["direct_page_union"] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12,
                                      "workspace_GiB": dws.numel() / 2 ** 30}
         del dws
+        arms["selector"] = selector_arm(pw, torch, wl, dev, shp, O, ws)
 
     swp = sweep(pw, torch, wl, inp, dev, shp, O, ws) if args.sweep else None
 

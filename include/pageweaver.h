@@ -181,6 +181,40 @@ pw_status pw_dense_union_ref(const pw_shape* shape, const uint16_t* Q,
                              uint16_t* O, void* ws, size_t ws_bytes,
                              void* stream);
 
+/* ---------------------------------------------------------------------------
+ * pw_select -- a synthetic dynamic page selector producing sel_pages.
+ *
+ * [abs]: dynamic sparse attention gives every query its own set of selected
+ * KV pages; the method takes that relation as given.  This call is a
+ * stand-in selector (our own rule, in the block-sparse style) that derives
+ * the relation from Q and K so the path can run on model-like selections.
+ *
+ * For KV head h and query t with own page p = t / P:
+ *   fixed pages   0 and p, p-1, ..., p-n_local+1 (those >= 0);
+ *   candidates    pages 1..p that are not fixed;
+ *   score(u)      k_scale[u][h] * sum_d qs[d] * C_u[d], where qs is the sum of
+ *                 the query's G head rows of Q and C_u[d] the sum over the
+ *                 page's keys of e4m3fn(K[u][h][j][d]);
+ *   the min(S - |fixed|, |candidates|) highest-scoring candidates are chosen
+ *   (ties to the lower page); sel_pages[h][t] lists fixed and chosen pages in
+ *   ascending order, padded with -1.
+ * Scores are computed on the matrix cores from bf16 hi/lo parts of qs and C
+ * (relative error about 2^-16 of sum_d |qs[d] C_u[d]|) with fp32 accumulation;
+ * pages whose scores differ by less than that may be chosen either way.
+ *
+ * In : Q, K_fp8, scales (layouts above; the V half of scales is unused),
+ *      n_local in [1, S - 1].
+ * Out: sel_pages int32 [H_kv][T][S] (every entry written).
+ * Support set: D in {64, 128}; P in {16, 32, 64}; N_pages <= 1024.
+ * Workspace: pw_select_workspace_bytes(shape) = 4 * (T + N_pages) * D bytes of
+ * bf16 operands plus T * N_pages * 4 bytes of scores (one KV head at a time),
+ * 256-byte aligned, required.
+ * ------------------------------------------------------------------------- */
+size_t pw_select_workspace_bytes(const pw_shape* shape);
+pw_status pw_select(const pw_shape* shape, const uint16_t* Q, const uint8_t* K_fp8,
+                    const float* scales, int32_t n_local, int32_t* sel_pages, void* ws,
+                    size_t ws_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* pw_status_string(pw_status status);
 /* Detail of the last non-OK status returned on the calling thread ("" if none). */

@@ -144,4 +144,34 @@ pw_status pw_dense_union_ref(const pw_shape* shape, const uint16_t* Q, const uin
                     "pw_dense_union_ref launch");
 }
 
+size_t pw_select_workspace_bytes(const pw_shape* shape) {
+  if (check_shape(shape) != PW_OK) return 0;
+  return pw::select_workspace(*shape);
+}
+
+pw_status pw_select(const pw_shape* shape, const uint16_t* Q, const uint8_t* K_fp8,
+                    const float* scales, int32_t n_local, int32_t* sel_pages, void* ws,
+                    size_t ws_bytes, void* stream) {
+  pw_status st = check_shape(shape);
+  if (st != PW_OK) return st;
+  if (!Q || !K_fp8 || !scales || !sel_pages)
+    return fail(PW_ERR_NULL, "Q, K_fp8, scales and sel_pages are required");
+  if (shape->D != 64 && shape->D != 128)
+    return fail(PW_ERR_UNSUPPORTED, "D = %d not in {64, 128}", shape->D);
+  if (shape->P != 16 && shape->P != 32 && shape->P != 64)
+    return fail(PW_ERR_UNSUPPORTED, "P = %d not in {16, 32, 64}", shape->P);
+  if (shape->N_pages > 1024)
+    return fail(PW_ERR_UNSUPPORTED, "N_pages = %d exceeds 1024 for the selector", shape->N_pages);
+  if (n_local < 1 || n_local + 1 > shape->S)
+    return fail(PW_ERR_UNSUPPORTED, "n_local = %d needs 1 <= n_local <= S - 1 (S = %d)", n_local,
+                shape->S);
+  const size_t need = pw::select_workspace(*shape);
+  if (!ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
+  if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (((uintptr_t)ws & 255) != 0) return fail(PW_ERR_DIMS, "workspace must be 256-byte aligned");
+  return hip_status(pw::launch_select(*shape, Q, K_fp8, scales, n_local, sel_pages, ws,
+                                      (hipStream_t)stream),
+                    "pw_select launch");
+}
+
 }  // extern "C"

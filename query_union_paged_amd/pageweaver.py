@@ -48,6 +48,8 @@ _SIGS = {
     "pw_group": (_i32, [_SHP, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
     "pw_union_attention_workspace_bytes": (_sz, [_SHP, _i32]),
     "pw_union_attention": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "pw_select_workspace_bytes": (_sz, [_SHP]),
+    "pw_select": (_i32, [_SHP, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "pw_dense_union_ref_workspace_bytes": (_sz, [_SHP]),
     "pw_dense_union_ref": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "pw_status_string": (ctypes.c_char_p, [_i32]),
@@ -136,6 +138,29 @@ def pw_union_attention(shp: PWShape, Q, K_fp8, V_fp8, scales, sel_pages, query_i
     _check(_lib.pw_union_attention(ctypes.byref(shp), q, k, v, sc, sel, ids, g, o, ws,
                                    workspace.numel(), _stream(stream)), "pw_union_attention")
     return O
+
+
+def pw_select_workspace_bytes(shp: PWShape) -> int:
+    return int(_lib.pw_select_workspace_bytes(ctypes.byref(shp)))
+
+
+def pw_select(shp: PWShape, Q, K_fp8, scales, n_local: int,
+              sel_pages: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+              stream=None) -> torch.Tensor:
+    """Synthetic page selection (sink, n_local local pages, top pages by block key sums)."""
+    N = shp.N_pages
+    q = _dev(Q, "Q", _BF16, (shp.T, shp.H_q, shp.D))
+    k = _dev(K_fp8, "K_fp8", _U8, (N, shp.H_kv, shp.P, shp.D))
+    sc = _dev(scales, "scales", (torch.float32,), (2, N, shp.H_kv))
+    if sel_pages is None:
+        sel_pages = torch.empty((shp.H_kv, shp.T, shp.S), dtype=torch.int32, device=Q.device)
+    sel = _dev(sel_pages, "sel_pages", (torch.int32,), (shp.H_kv, shp.T, shp.S))
+    if workspace is None:
+        workspace = torch.empty(pw_select_workspace_bytes(shp), dtype=torch.uint8, device=Q.device)
+    ws = _dev(workspace, "workspace", (torch.uint8,))
+    _check(_lib.pw_select(ctypes.byref(shp), q, k, sc, n_local, sel, ws, workspace.numel(),
+                          _stream(stream)), "pw_select")
+    return sel_pages
 
 
 def pw_dense_union_ref_workspace_bytes(shp: PWShape) -> int:

@@ -94,6 +94,21 @@ def test_dense_union_validation():
         assert f(ctypes.byref(shp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None) == pw.PW_ERR_NULL
 
 
+def test_select_validation():
+    f = pw._lib.pw_select
+    shp = _shape(S=8)
+    need = pw._lib.pw_select_workspace_bytes(ctypes.byref(shp))
+    assert need == 2 * (1024 * 64 * 2) + 2 * (64 * 64 * 2) + 1024 * 64 * 4   # bf16 hi/lo qs, C; fp32 scores
+    assert f(ctypes.byref(shp), None, FAKE, FAKE, 2, FAKE, FAKE, need, None) == pw.PW_ERR_NULL
+    assert f(ctypes.byref(shp), FAKE, FAKE, FAKE, 0, FAKE, FAKE, need, None) == pw.PW_ERR_UNSUPPORTED
+    assert f(ctypes.byref(shp), FAKE, FAKE, FAKE, 8, FAKE, FAKE, need, None) == pw.PW_ERR_UNSUPPORTED
+    assert f(ctypes.byref(_shape(D=96)), FAKE, FAKE, FAKE, 2, FAKE, FAKE, need, None) == pw.PW_ERR_UNSUPPORTED
+    big = _shape(T=2048 * 16, N_pages=2048)
+    assert f(ctypes.byref(big), FAKE, FAKE, FAKE, 2, FAKE, FAKE, 1 << 40, None) == pw.PW_ERR_UNSUPPORTED
+    assert f(ctypes.byref(shp), FAKE, FAKE, FAKE, 2, FAKE, FAKE, need - 1, None) == pw.PW_ERR_WORKSPACE
+    assert f(ctypes.byref(shp), FAKE, FAKE, FAKE, 2, FAKE, None, need, None) == pw.PW_ERR_NULL
+
+
 def test_binding_refuses_host_tensors():
     import torch
     shp = _shape()
