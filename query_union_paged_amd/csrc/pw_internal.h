@@ -13,8 +13,6 @@ typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8;
 
-constexpr int kWave = 64;
-
 // Make this wave's earlier LDS writes visible to its later LDS reads (the
 // lanes of one wave exchange data through LDS without a workgroup barrier).
 __device__ __forceinline__ void wave_sync() {
@@ -29,11 +27,6 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
   return v;
 }
 
-__device__ __forceinline__ int lane_prefix(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                   __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0));
-}
-
 // Eight e4m3fn bytes (two dwords) -> eight bf16, exactly (every e4m3fn value,
 // subnormals included, is a bf16 value).
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
@@ -43,10 +36,6 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
   bf16x8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
   return r;
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
-  return __builtin_bit_cast(bf16x8, v);
 }
 
 // Host-side launchers (implemented next to their kernels).

@@ -46,9 +46,7 @@ constexpr float kTau = 8.0f;   // lazy-rescale threshold (log2 units): p <= 2^8
 
 struct UAParams {
   const uint16_t* Q;
-  const uint8_t* K;
-  const uint8_t* V;
-  const uint8_t* Kt;   // tiled copies (see tile_kv_kernel)
+  const uint8_t* Kt;   // tiled copies of the FP8 K and V pages (see tile_kv_kernel)
   const uint8_t* Vt;
   const float* scales;
   const int32_t* sel;
@@ -570,10 +568,9 @@ hipError_t launch_d(const UAParams& prm, int blocks, size_t lds, hipStream_t str
   return hipGetLastError();
 }
 
-void common_params(UAParams& prm, const pw_shape& s, const uint16_t* Q, const uint8_t* K,
-                   const uint8_t* V, const float* scales) {
+void common_params(UAParams& prm, const pw_shape& s, const uint16_t* Q, const float* scales) {
   prm = UAParams{};
-  prm.Q = Q; prm.K = K; prm.V = V; prm.scales = scales;
+  prm.Q = Q; prm.scales = scales;
   prm.T = s.T; prm.Hq = s.H_q; prm.Hkv = s.H_kv; prm.G = s.H_q / s.H_kv; prm.P = s.P;
   prm.N = s.N_pages; prm.S = s.S;
   prm.qk_scale = kLog2e / sqrtf((float)s.D);
@@ -603,7 +600,7 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
   hipError_t e = tile_kv(s, K, V, tiles, stream);
   if (e != hipSuccess) return e;
   UAParams prm;
-  common_params(prm, s, Q, K, V, scales);
+  common_params(prm, s, Q, scales);
   prm.Kt = tiles;
   prm.Vt = tiles + tiled_kv_bytes(s) / 2;
   prm.sel = sel; prm.ids = ids; prm.O = O; prm.g = g;
@@ -624,7 +621,7 @@ hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uin
                                  const float* scales, const int2* plist, const int* pcount,
                                  float* partials, int Np, int Tc, int t0, hipStream_t stream) {
   UAParams prm;
-  common_params(prm, s, Q, nullptr, nullptr, scales);
+  common_params(prm, s, Q, scales);
   prm.Kt = tiles;
   prm.Vt = tiles + tiled_kv_bytes(s) / 2;
   prm.plist = plist; prm.pcount = pcount; prm.partials = partials;
