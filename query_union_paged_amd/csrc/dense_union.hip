@@ -13,11 +13,11 @@
 //      bitset in LDS, walks its pairs (2k, 2k+1) in ascending order and appends
 //      (query, partial slot, which pages) to pair k's list -- the pair's full
 //      membership; an entry with both pages is on the common list, one page
-//      on an exclusive list;
+//      on an exclusive list; list ranges are reserved once per (wave, pair);
 //   3. pair attention (union_attn.hip, pair mode): tiles of 8 entries of a
 //      list compute (m, l, acc) over their own visible keys of the pair;
 //   4. merge_kernel: one wave per (KV head, query) combines its partials by
-//      log-sum-exp into O.
+//      log-sum-exp into O (maximum first, then independent weighted loads).
 // The list order within a pair depends on atomics, but every partial has a
 // fixed slot and a row's arithmetic does not depend on the other rows of its
 // tile, so the result is deterministic.
@@ -61,39 +61,67 @@ __global__ void zero_kernel(int* p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
 }
 
+// One wave per 64 queries of one KV head.  Each lane sets its query's page bitset
+// in LDS and walks its pairs (2k, 2k+1) in ascending order.  The wave first
+// counts its entries per pair in LDS, reserves one range per pair in the global
+// list (one atomic per (wave, pair) instead of one per entry: the sink and
+// local pairs are in every query's support), then writes its entries there.
 __global__ __launch_bounds__(64) void pair_entries_kernel(const int32_t* __restrict__ sel, int T,
                                                          int S, int N, int NW, int Np, int Tc,
                                                          int maxp, int t0, int* pcount,
                                                          int* npairs, int2* plist) {
-  extern __shared__ uint32_t words[];              // [64][NW + 1]
-  const int h = blockIdx.y;
-  const int tl = blockIdx.x * 64 + threadIdx.x;    // query within the chunk
+  extern __shared__ uint32_t sh[];                 // [64][NW + 1] bitsets, cnt[Np], pos[Np]
+  const int h = blockIdx.y, lane = threadIdx.x;
+  const int tl = blockIdx.x * 64 + lane;           // query within the chunk
   const int t = t0 + tl;
-  uint32_t* w = words + threadIdx.x * (NW + 1);
+  uint32_t* w = sh + lane * (NW + 1);
+  int* cnt = reinterpret_cast<int*>(sh + 64 * (NW + 1));
+  int* pos = cnt + Np;
   for (int i = 0; i < NW; ++i) w[i] = 0;
-  if (tl >= Tc || t >= T) return;
-  const int32_t* row = sel + ((size_t)h * T + t) * S;
-  for (int s = 0; s < S; ++s) {
-    const int u = row[s];
-    if (u >= 0 && u < N) w[u >> 5] |= 1u << (u & 31);
-  }
-  int j = 0;
-  for (int i = 0; i < NW; ++i) {
-    const uint32_t x = w[i];
-    uint32_t pm = (x | (x >> 1)) & 0x55555555u;    // pairs with at least one page
-    while (pm) {
-      const int bit = __builtin_ctz(pm);
-      pm &= pm - 1;
-      const int k = i * 16 + (bit >> 1);
-      const int kind = (x >> bit) & 3;             // 1: page 2k, 2: page 2k+1, 3: both
-      const int slot = (h * Tc + tl) * maxp + j++;
-      const int pos = atomicAdd(&pcount[h * Np + k], 1);
-      plist[((size_t)h * Np + k) * Tc + pos] = make_int2(tl, slot | (kind << 30));
+  for (int k = lane; k < Np; k += 64) cnt[k] = 0;
+  const bool ok = tl < Tc && t < T;
+  if (ok) {
+    const int32_t* row = sel + ((size_t)h * T + t) * S;
+    for (int s2 = 0; s2 < S; ++s2) {
+      const int u = row[s2];
+      if (u >= 0 && u < N) w[u >> 5] |= 1u << (u & 31);
     }
   }
-  npairs[h * Tc + tl] = j;
+  wave_sync();
+  // f(k, kind) for every pair of this lane's query, ascending
+  auto for_pairs = [&](auto&& f) {
+    for (int i = 0; i < NW; ++i) {
+      const uint32_t x = w[i];
+      uint32_t pm = (x | (x >> 1)) & 0x55555555u;  // pairs with at least one page
+      while (pm) {
+        const int bit = __builtin_ctz(pm);
+        pm &= pm - 1;
+        f(i * 16 + (bit >> 1), (int)((x >> bit) & 3));   // kind 1: page 2k, 2: 2k+1, 3: both
+      }
+    }
+  };
+  if (ok) for_pairs([&](int k, int) { atomicAdd(&cnt[k], 1); });
+  wave_sync();
+  for (int k = lane; k < Np; k += 64) {
+    const int c = cnt[k];
+    pos[k] = c ? atomicAdd(&pcount[h * Np + k], c) : 0;
+  }
+  wave_sync();
+  if (ok) {
+    int j = 0;
+    for_pairs([&](int k, int kind) {
+      const int slot = (h * Tc + tl) * maxp + j++;
+      const int at = atomicAdd(&pos[k], 1);
+      plist[((size_t)h * Np + k) * Tc + at] = make_int2(tl, slot | (kind << 30));
+    });
+    npairs[h * Tc + tl] = j;
+  }
 }
 
+// One wave per (KV head, query).  For each of the G heads: the partials'
+// (m, l) are read one per lane, their maximum M fixes the weights
+// w_i = 2^(m_i - M), and every lane accumulates its d values over the
+// partials with independent loads (no serial running-max chain).
 template <int D>
 __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ partials,
                                                    const int* __restrict__ npairs,
@@ -108,19 +136,35 @@ __global__ __launch_bounds__(64) void merge_kernel(const float* __restrict__ par
   const int n = npairs[h * Tc + tl];
   const size_t slot0 = ((size_t)h * Tc + tl) * maxp;
   for (int j = 0; j < G; ++j) {
-    float M = -INFINITY, L = 0.f, A[PER];
+    auto part = [&](int i) { return partials + ((slot0 + i) * G + j) * (D + 4); };
+    float M = -INFINITY;
+    for (int i = lane; i < n; i += 64) {
+      const float* pp = part(i);
+      if (pp[1] > 0.f) M = fmaxf(M, pp[0]);        // l > 0: the pair had a visible key
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+    float L = 0.f, A[PER];
 #pragma unroll
     for (int q = 0; q < PER; ++q) A[q] = 0.f;
-    for (int jj = 0; jj < n; ++jj) {
-      const float* pp = partials + ((slot0 + jj) * G + j) * (D + 4);
-      const float m = pp[0], l = pp[1];
-      if (!(l > 0.f)) continue;                    // no visible key in this pair
-      const float Mn = fmaxf(M, m);
-      const float a = exp2f(M - Mn), c = exp2f(m - Mn);
-      L = L * a + l * c;
+    if (M > -INFINITY) {
+      for (int i0 = 0; i0 < n; i0 += 64) {
+        float wgt = 0.f;
+        if (i0 + lane < n) {
+          const float* pp = part(i0 + lane);
+          wgt = (pp[1] > 0.f) ? exp2f(pp[0] - M) : 0.f;
+          L += wgt * pp[1];
+        }
+        const int cnt = min(64, n - i0);
+        for (int r = 0; r < cnt; ++r) {
+          const float wr = __shfl(wgt, r);
+          const float* pp = part(i0 + r);
 #pragma unroll
-      for (int q = 0; q < PER; ++q) A[q] = A[q] * a + pp[4 + lane + 64 * q] * c;
-      M = Mn;
+          for (int q = 0; q < PER; ++q) A[q] += wr * pp[4 + lane + 64 * q];
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) L += __shfl_xor(L, off);
     }
     const float inv = (L > 0.f) ? 1.f / L : 0.f;
     uint16_t* op = O + ((size_t)t * Hq + h * G + j) * D;
@@ -156,7 +200,8 @@ hipError_t launch_dense_union(const pw_shape& s, const uint16_t* Q, const uint8_
                        n_count);
     const int tcur = (s.T - t0 < d.Tc) ? s.T - t0 : d.Tc;
     hipLaunchKernelGGL(pair_entries_kernel, dim3((tcur + 63) / 64, s.H_kv), dim3(64),
-                       (size_t)64 * (d.NW + 1) * 4, stream, sel, s.T, s.S, s.N_pages, d.NW, d.Np,
+                       ((size_t)64 * (d.NW + 1) + 2 * (size_t)d.Np) * 4, stream, sel, s.T, s.S,
+                       s.N_pages, d.NW, d.Np,
                        d.Tc, d.maxp, t0, pcount, npairs, plist);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
