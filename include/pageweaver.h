@@ -115,6 +115,24 @@ pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W,
                    void* stream);
 
 /* ---------------------------------------------------------------------------
+ * pw_check_ids -- is every query_ids row a permutation of 0..T-1?
+ *
+ * pw_union_attention writes exactly the rows listed in query_ids; with a row
+ * that is not a permutation, unlisted outputs stay unwritten.  This optional
+ * device-side check lets a caller verify IDs that did not come from pw_group
+ * without a host round trip of its own.
+ *
+ * Out: bad_counts int32 [H_kv] (device): per KV head, the number of entries
+ * that are outside [0, T) or repeat an earlier entry of the row; every count
+ * is 0 exactly when every row is a permutation.  Enqueued on `stream`.
+ * Workspace: pw_check_ids_workspace_bytes(shape) = ceil(H_kv * T / 32) * 4
+ * bytes, required.
+ * ------------------------------------------------------------------------- */
+size_t pw_check_ids_workspace_bytes(const pw_shape* shape);
+pw_status pw_check_ids(const pw_shape* shape, const int32_t* query_ids, int32_t* bad_counts,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * pw_union_attention -- ID-aware union attention.
  *
  * [abs]: query unions share page loads and fill matrix-core tiles; each query

@@ -91,6 +91,23 @@ pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W, i
                     "pw_group launch");
 }
 
+size_t pw_check_ids_workspace_bytes(const pw_shape* shape) {
+  if (check_shape(shape) != PW_OK) return 0;
+  return pw::check_ids_workspace(*shape);
+}
+
+pw_status pw_check_ids(const pw_shape* shape, const int32_t* query_ids, int32_t* bad_counts,
+                       void* ws, size_t ws_bytes, void* stream) {
+  pw_status st = check_shape(shape);
+  if (st != PW_OK) return st;
+  if (!query_ids || !bad_counts) return fail(PW_ERR_NULL, "query_ids and bad_counts are required");
+  const size_t need = pw::check_ids_workspace(*shape);
+  if (!ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
+  if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  return hip_status(pw::launch_check_ids(*shape, query_ids, bad_counts, ws, (hipStream_t)stream),
+                    "pw_check_ids launch");
+}
+
 size_t pw_union_attention_workspace_bytes(const pw_shape* shape, int32_t) {
   if (check_shape(shape) != PW_OK) return 0;
   return pw::tiled_kv_bytes(*shape);

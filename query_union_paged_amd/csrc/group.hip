@@ -255,3 +255,50 @@ hipError_t launch_group(const pw_shape& s, const int32_t* sel, int W, int g, int
 }
 
 }  // namespace pw
+
+// ---- query-ID check: per KV head, the number of entries that are out of
+// range or repeat an earlier ID (0 for every head <=> each row is a permutation).
+namespace pw {
+namespace {
+
+__global__ void ids_zero_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+__global__ void ids_check_kernel(const int32_t* __restrict__ ids, int T, int Hkv,
+                                 uint32_t* __restrict__ seen, int32_t* __restrict__ bad) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (size_t)T * Hkv) return;
+  const int h = (int)(i / T);
+  const int t = ids[i];
+  bool wrong = t < 0 || t >= T;
+  if (!wrong) {
+    const size_t bit = (size_t)h * T + t;
+    wrong = (atomicOr(&seen[bit >> 5], 1u << (bit & 31)) >> (bit & 31)) & 1u;
+  }
+  if (wrong) atomicAdd(&bad[h], 1);
+}
+
+}  // namespace
+
+size_t check_ids_workspace(const pw_shape& s) {
+  return ((size_t)s.H_kv * s.T + 31) / 32 * 4;
+}
+
+hipError_t launch_check_ids(const pw_shape& s, const int32_t* ids, int32_t* bad, void* ws,
+                            hipStream_t stream) {
+  uint32_t* seen = static_cast<uint32_t*>(ws);
+  const size_t nw = check_ids_workspace(s) / 4;
+  hipLaunchKernelGGL(ids_zero_kernel, dim3((unsigned)((nw + 255) / 256)), dim3(256), 0, stream,
+                     seen, nw);
+  hipLaunchKernelGGL(ids_zero_kernel, dim3(1), dim3(64), 0, stream,
+                     reinterpret_cast<uint32_t*>(bad), (size_t)s.H_kv);
+  const size_t n = (size_t)s.H_kv * s.T;
+  hipLaunchKernelGGL(ids_check_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream,
+                     ids, s.T, s.H_kv, seen, bad);
+  return hipGetLastError();
+}
+
+}  // namespace pw

@@ -52,6 +52,9 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
 hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* tiles,
                                  const float* scales, const int2* plist, const int* pcount,
                                  float* partials, int Np, int Tc, int t0, hipStream_t stream);
+size_t check_ids_workspace(const pw_shape& s);
+hipError_t launch_check_ids(const pw_shape& s, const int32_t* ids, int32_t* bad, void* ws,
+                            hipStream_t stream);
 size_t select_workspace(const pw_shape& s);
 hipError_t launch_select(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
                          const float* scales, int L, int32_t* sel, void* ws, hipStream_t stream);

@@ -48,6 +48,8 @@ _SIGS = {
     "pw_group": (_i32, [_SHP, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
     "pw_union_attention_workspace_bytes": (_sz, [_SHP, _i32]),
     "pw_union_attention": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "pw_check_ids_workspace_bytes": (_sz, [_SHP]),
+    "pw_check_ids": (_i32, [_SHP, _vp, _vp, _vp, _sz, _vp]),
     "pw_select_workspace_bytes": (_sz, [_SHP]),
     "pw_select": (_i32, [_SHP, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "pw_dense_union_ref_workspace_bytes": (_sz, [_SHP]),
@@ -138,6 +140,17 @@ def pw_union_attention(shp: PWShape, Q, K_fp8, V_fp8, scales, sel_pages, query_i
     _check(_lib.pw_union_attention(ctypes.byref(shp), q, k, v, sc, sel, ids, g, o, ws,
                                    workspace.numel(), _stream(stream)), "pw_union_attention")
     return O
+
+
+def pw_check_ids(shp: PWShape, query_ids: torch.Tensor, stream=None) -> torch.Tensor:
+    """Per KV head, the number of out-of-range or repeated IDs (all zero: permutations)."""
+    ids = _dev(query_ids, "query_ids", (torch.int32,), (shp.H_kv, shp.T))
+    bad = torch.empty((shp.H_kv,), dtype=torch.int32, device=query_ids.device)
+    ws = torch.empty(int(_lib.pw_check_ids_workspace_bytes(ctypes.byref(shp))), dtype=torch.uint8,
+                     device=query_ids.device)
+    _check(_lib.pw_check_ids(ctypes.byref(shp), ids, bad.data_ptr(), ws.data_ptr(), ws.numel(),
+                             _stream(stream)), "pw_check_ids")
+    return bad
 
 
 def pw_select_workspace_bytes(shp: PWShape) -> int:

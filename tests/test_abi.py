@@ -109,6 +109,16 @@ def test_select_validation():
     assert f(ctypes.byref(shp), FAKE, FAKE, FAKE, 2, FAKE, None, need, None) == pw.PW_ERR_NULL
 
 
+def test_check_ids_validation():
+    f = pw._lib.pw_check_ids
+    shp = _shape(H_kv=2, H_q=4)
+    need = pw._lib.pw_check_ids_workspace_bytes(ctypes.byref(shp))
+    assert need == (2 * 1024 + 31) // 32 * 4
+    assert f(ctypes.byref(shp), None, FAKE, FAKE, need, None) == pw.PW_ERR_NULL
+    assert f(ctypes.byref(shp), FAKE, FAKE, None, need, None) == pw.PW_ERR_NULL
+    assert f(ctypes.byref(shp), FAKE, FAKE, FAKE, need - 1, None) == pw.PW_ERR_WORKSPACE
+
+
 def test_binding_refuses_host_tensors():
     import torch
     shp = _shape()

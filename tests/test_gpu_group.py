@@ -89,3 +89,24 @@ def test_group_golden_cases():
         full[0, :T] = sel
         got = _gpu_ids(full, n_abi, p_abi, W, g)
         assert got[0, :T].tolist() == case["expected"], case["name"]
+
+
+def test_check_ids_counts():
+    # permutations give 0; out-of-range entries and repeats are counted per KV head
+    from query_union_paged_amd import pageweaver as pw
+    log("[case] pw_check_ids")
+    wl = synth.WORKLOADS["prefill_8k"]
+    sel = torch.from_numpy(host_inputs("prefill_8k")["sel_pages"]).cuda()
+    shp = pw.shape(*wl.shape_tuple())
+    ids = pw.pw_group(shp, sel, wl.W, wl.g)
+    assert pw.pw_check_ids(shp, ids).cpu().tolist() == [0] * wl.H_kv
+    bad = ids.clone()
+    bad[1, 5] = bad[1, 6]            # one repeat
+    bad[3, 0] = -1                   # out of range
+    bad[3, 1] = wl.T                 # out of range
+    bad[3, 2] = bad[3, 3] = bad[3, 4]   # two repeats of one ID
+    got = pw.pw_check_ids(shp, bad).cpu().numpy()
+    b = bad.cpu().numpy()
+    want = [int(((r < 0) | (r >= wl.T)).sum()) + int(((r >= 0) & (r < wl.T)).sum()) -
+            len(set(r[(r >= 0) & (r < wl.T)].tolist())) for r in b]
+    assert got.tolist() == want == [0, 1, 0, 4, 0, 0, 0, 0]
