@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--gen-workers", type=int, default=16,
                     help="processes for input generation (0: in-process, e.g. under a profiler)")
     ap.add_argument("--sweep", action="store_true",
-                    help="also time the complete call over W in {32..256} x g in {4, 8, 16} "
+                    help="also time the complete call over W in {32..1024} x g in {4, 8, 16} "
                          "(regrouped, and identity grouping at each g)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="after the timed region, one plain 1 GiB device-to-device copy "
@@ -162,7 +162,7 @@ def sweep(pw, torch, wl, inp, dev, shp, O, ws, reps: int = 5):
         u_id = union_stats(inp["sel_pages"], ident.cpu().numpy(), g, wl.N)
         rows.append({"W": None, "g": g, "grouping": "identity", "search_ms": 0.0,
                      "attention_ms": a_id, "call_ms": a_id, "union_pages_mean": float(u_id.mean())})
-        for W in (32, 64, 128, 256):
+        for W in (32, 64, 128, 256, 512, 1024):
             if W < g:
                 continue
             s_ms = timed(lambda: pw.pw_group(shp, dev["sel_pages"], W, g, query_ids=ids))

@@ -105,7 +105,7 @@ typedef struct pw_shape {
  * written window by window, group by group, members in insertion order.  The
  * result is unique, so it is bit-exact against any correct implementation.
  *
- * In : sel_pages (see layouts), W in [1, 256], g in [1, 16].
+ * In : sel_pages (see layouts), W in [1, 1024], g in [1, 16].
  * Out: query_ids int32 [H_kv][T] (every entry written).
  * Support set: N_pages <= 1024.  Workspace: none (returns 0).
  * ------------------------------------------------------------------------- */

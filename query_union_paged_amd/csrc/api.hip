@@ -83,7 +83,7 @@ pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W, i
   pw_status st = check_shape(shape);
   if (st != PW_OK) return st;
   if (!sel_pages || !query_ids) return fail(PW_ERR_NULL, "sel_pages and query_ids are required");
-  if (W < 1 || W > 256) return fail(PW_ERR_UNSUPPORTED, "W = %d outside [1, 256]", W);
+  if (W < 1 || W > 1024) return fail(PW_ERR_UNSUPPORTED, "W = %d outside [1, 1024]", W);
   if (g < 1 || g > 16) return fail(PW_ERR_UNSUPPORTED, "g = %d outside [1, 16]", g);
   if (shape->N_pages > 1024)
     return fail(PW_ERR_UNSUPPORTED, "N_pages = %d exceeds 1024 for the search", shape->N_pages);

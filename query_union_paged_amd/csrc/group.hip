@@ -55,17 +55,23 @@ __device__ __forceinline__ uint32_t wave_or(uint32_t v) {
 // candidates at a time (LDS `stage`) and kept in registers compacted to the
 // window's active words (word jj = the jj-th word any candidate uses; words
 // past the active count are zero for every candidate and cost nothing).
-template <int C, int NWB>
+// With NWV > 1 waves per window (W > 256), wave wv owns candidates
+// 256 wv + 64 c + lane; each step then takes the minimum over the waves' minima
+// through LDS (`xch`), and the owner of the chosen candidate publishes its
+// words there (two workgroup barriers per step).
+template <int C, int NWB, int NWV>
 __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, int S, int N,
                                             int Wr, int g, uint32_t act, uint32_t* stage,
-                                            int* order) {
-  const int lane = threadIdx.x;
+                                            int* order, uint32_t* xch) {
+  const int lane = threadIdx.x & 63;
+  const int wv = NWV > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+  const int cbase = 256 * wv;                // first candidate of this wave
   uint32_t b[C][NWB];
   // one 64-candidate chunk: bits set in LDS, then each lane takes its row
   auto build_chunk = [&](uint32_t(&bc)[NWB], const int c) __attribute__((always_inline)) {
     for (int i = lane; i < 64 * kStride; i += 64) stage[i] = 0;
     wave_sync();
-    const int r0 = 64 * c;
+    const int r0 = cbase + 64 * c;
     const int nrows = max(0, min(64, Wr - r0));
     const int32_t* base = wbase + (size_t)r0 * S;
     auto put = [&](int r, int u) __attribute__((always_inline)) {
@@ -117,18 +123,43 @@ __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, i
   uint32_t avail = 0;                      // bit c: candidate 64c + lane unassigned
 #pragma unroll
   for (int c = 0; c < C; ++c)
-    if (64 * c + lane < Wr) avail |= 1u << c;
+    if (cbase + 64 * c + lane < Wr) avail |= 1u << c;
   uint32_t U[NWB];                         // the group's union (wave-uniform)
   uint32_t w[NWB];                         // the chosen candidate's words
 
-  // the chosen candidate's words, read from its lane (wave-uniform result)
-  auto fetch = [&](int cb, int lb) __attribute__((always_inline)) {
+  // the chosen candidate's words, read from its lane (wave-uniform result);
+  // across waves the owner publishes them in LDS
+  auto fetch = [&](int wb, int cb, int lb) __attribute__((always_inline)) {
+    if (wb == wv) {
 #pragma unroll
-    for (int c = 0; c < C; ++c)
-      if (c == cb) {
+      for (int c = 0; c < C; ++c)
+        if (c == cb) {
 #pragma unroll
-        for (int jj = 0; jj < NWB; ++jj) w[jj] = __builtin_amdgcn_readlane(b[c][jj], lb);
+          for (int jj = 0; jj < NWB; ++jj) w[jj] = __builtin_amdgcn_readlane(b[c][jj], lb);
+        }
+    }
+    if constexpr (NWV > 1) {
+      uint32_t* row = xch + 4;   // [32]
+      if (wb == wv && lane == 0) {
+#pragma unroll
+        for (int jj = 0; jj < NWB; ++jj) row[jj] = w[jj];
       }
+      __syncthreads();
+#pragma unroll
+      for (int jj = 0; jj < NWB; ++jj) w[jj] = __builtin_amdgcn_readfirstlane(row[jj]);
+    }
+  };
+  // the window-wide minimum of a key (the wave's own minimum when NWV == 1)
+  auto window_min = [&](uint32_t key) __attribute__((always_inline)) -> uint32_t {
+    uint32_t m = __builtin_amdgcn_readfirstlane(wave_min_dpp(key));
+    if constexpr (NWV > 1) {
+      if (lane == 0) xch[wv] = m;
+      __syncthreads();
+#pragma unroll
+      for (int v = 0; v < NWV; ++v) m = min(m, xch[v]);
+      m = __builtin_amdgcn_readfirstlane(m);
+    }
+    return m;
   };
   // every candidate gains the pages of delta in word jj
   auto add_gain = [&](int jj, uint32_t delta) __attribute__((always_inline)) {
@@ -142,13 +173,13 @@ __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, i
     uint32_t key = kNone;
 #pragma unroll
     for (int c = 0; c < C; ++c)
-      if ((avail >> c) & 1u) key = min(key, (uint32_t)(64 * c + lane));
-    uint32_t best = __builtin_amdgcn_readfirstlane(wave_min_dpp(key));
-    int cb = best >> 6, lb = best & 63;
-    if (lane == lb) avail &= ~(1u << cb);
-    if (lane == 0) order[pos] = (int)best;
+      if ((avail >> c) & 1u) key = min(key, (uint32_t)(cbase + 64 * c + lane));
+    uint32_t best = window_min(key);
+    int wb = best >> 8, cb = (best >> 6) & 3, lb = best & 63;
+    if (wb == wv && lane == lb) avail &= ~(1u << cb);
+    if (wv == 0 && lane == 0) order[pos] = (int)best;
     ++pos;
-    fetch(cb, lb);
+    fetch(wb, cb, lb);
 #pragma unroll
     for (int c = 0; c < C; ++c) gain[c] = 0;
 #pragma unroll
@@ -162,14 +193,15 @@ __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, i
 #pragma unroll
       for (int c = 0; c < C; ++c)
         if ((avail >> c) & 1u)
-          key = min(key, ((tot[c] - gain[c]) << 10) | (uint32_t)(64 * c + lane));
-      best = __builtin_amdgcn_readfirstlane(wave_min_dpp(key) & 1023u);
-      cb = best >> 6;
+          key = min(key, ((tot[c] - gain[c]) << 10) | (uint32_t)(cbase + 64 * c + lane));
+      best = window_min(key) & 1023u;
+      wb = best >> 8;
+      cb = (best >> 6) & 3;
       lb = best & 63;
-      if (lane == lb) avail &= ~(1u << cb);
-      if (lane == 0) order[pos] = (int)best;
+      if (wb == wv && lane == lb) avail &= ~(1u << cb);
+      if (wv == 0 && lane == 0) order[pos] = (int)best;
       ++pos;
-      fetch(cb, lb);
+      fetch(wb, cb, lb);
 #pragma unroll
       for (int jj = 0; jj < NWB; ++jj) {
         const uint32_t d = w[jj] & ~U[jj];
@@ -182,25 +214,31 @@ __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, i
   }
 }
 
-template <int C>
-__global__ __launch_bounds__(64) void group_kernel(const int32_t* __restrict__ sel,
-                                                   int32_t* __restrict__ ids, int T, int S,
-                                                   int N, int W, int g, int n_windows) {
+// blockDim = 64 NWV: one wave per window (NWV = 1, W <= 256) or NWV waves
+// of 256 candidates each (W <= 1024).
+template <int C, int NWV>
+__global__ __launch_bounds__(64 * NWV) void group_kernel(const int32_t* __restrict__ sel,
+                                                         int32_t* __restrict__ ids, int T, int S,
+                                                         int N, int W, int g, int n_windows) {
   extern __shared__ uint32_t lds[];
-  uint32_t* stage = lds;                                   // [64][kStride] one chunk's bitsets
-  int* order = reinterpret_cast<int*>(lds + 64 * kStride); // [C * 64] emission order
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wv = NWV > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
+  uint32_t* stage = lds + wv * 64 * kStride;                      // [64][kStride] per wave
+  int* order = reinterpret_cast<int*>(lds + NWV * 64 * kStride);  // [NWV C 64] emission order
+  uint32_t* xch = lds + NWV * 64 * kStride + NWV * C * 64;        // [4 keys | 32 words | 4 act]
   const int h = blockIdx.x / n_windows;
   const int w0 = (blockIdx.x % n_windows) * W;
   const int Wr = min(W, T - w0);
   const int32_t* wbase = sel + ((size_t)h * T + w0) * S;
+  // this wave's candidate rows
+  const int r_lo = min(Wr, 256 * wv), r_hi = min(Wr, 256 * wv + 64 * C);
 
   // words (32 pages each) that some candidate of the window uses
   uint32_t act = 0;
   if ((S & 3) == 0) {
-    const int n4 = (Wr * S) >> 2;
+    const int lo4 = (r_lo * S) >> 2, n4 = (r_hi * S) >> 2;
     const int4* w4 = reinterpret_cast<const int4*>(wbase);
-    for (int i0 = 0; i0 < n4; i0 += 64 * 8) {
+    for (int i0 = lo4; i0 < n4; i0 += 64 * 8) {
       int4 v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -216,30 +254,41 @@ __global__ __launch_bounds__(64) void group_kernel(const int32_t* __restrict__ s
       }
     }
   } else {
-    for (int i = lane; i < Wr * S; i += 64) {
+    for (int i = r_lo * S + lane; i < r_hi * S; i += 64) {
       const int u = wbase[i];
       if (u >= 0 && u < N) act |= 1u << (u >> 5);
     }
   }
   act = wave_or(act);
+  if constexpr (NWV > 1) {
+    if (lane == 0) xch[36 + wv] = act;
+    __syncthreads();
+    act = 0;
+#pragma unroll
+    for (int v = 0; v < NWV; ++v) act |= xch[36 + v];
+    act = __builtin_amdgcn_readfirstlane(act);
+  }
   const int nact = __builtin_popcount(act);
   if (nact <= 8)
-    window_body<C, 8>(wbase, S, N, Wr, g, act, stage, order);
+    window_body<C, 8, NWV>(wbase, S, N, Wr, g, act, stage, order, xch);
   else if (nact <= 16)
-    window_body<C, 16>(wbase, S, N, Wr, g, act, stage, order);
+    window_body<C, 16, NWV>(wbase, S, N, Wr, g, act, stage, order, xch);
   else
-    window_body<C, 32>(wbase, S, N, Wr, g, act, stage, order);
-  wave_sync();
-  for (int i = lane; i < Wr; i += 64) ids[(size_t)h * T + w0 + i] = w0 + order[i];
+    window_body<C, 32, NWV>(wbase, S, N, Wr, g, act, stage, order, xch);
+  if constexpr (NWV > 1)
+    __syncthreads();
+  else
+    wave_sync();
+  for (int i = threadIdx.x; i < Wr; i += 64 * NWV) ids[(size_t)h * T + w0 + i] = w0 + order[i];
 }
 
-template <int C>
+template <int C, int NWV>
 hipError_t launch_c(const pw_shape& s, const int32_t* sel, int W, int g, int32_t* ids,
                     hipStream_t stream) {
   const int n_windows = (s.T + W - 1) / W;
-  const size_t lds = ((size_t)64 * kStride + (size_t)C * 64) * 4;
-  hipLaunchKernelGGL(group_kernel<C>, dim3(s.H_kv * n_windows), dim3(64), lds, stream, sel, ids,
-                     s.T, s.S, s.N_pages, W, g, n_windows);
+  const size_t lds = ((size_t)NWV * 64 * kStride + (size_t)NWV * C * 64 + 40) * 4;
+  hipLaunchKernelGGL((group_kernel<C, NWV>), dim3(s.H_kv * n_windows), dim3(64 * NWV), lds,
+                     stream, sel, ids, s.T, s.S, s.N_pages, W, g, n_windows);
   return hipGetLastError();
 }
 
@@ -248,10 +297,13 @@ hipError_t launch_c(const pw_shape& s, const int32_t* sel, int W, int g, int32_t
 hipError_t launch_group(const pw_shape& s, const int32_t* sel, int W, int g, int32_t* ids,
                         hipStream_t stream) {
   const int C = (W + 63) / 64;
-  if (C <= 1) return launch_c<1>(s, sel, W, g, ids, stream);
-  if (C == 2) return launch_c<2>(s, sel, W, g, ids, stream);
-  if (C == 3) return launch_c<3>(s, sel, W, g, ids, stream);
-  return launch_c<4>(s, sel, W, g, ids, stream);
+  if (C <= 1) return launch_c<1, 1>(s, sel, W, g, ids, stream);
+  if (C == 2) return launch_c<2, 1>(s, sel, W, g, ids, stream);
+  if (C == 3) return launch_c<3, 1>(s, sel, W, g, ids, stream);
+  if (C == 4) return launch_c<4, 1>(s, sel, W, g, ids, stream);
+  if (W <= 512) return launch_c<4, 2>(s, sel, W, g, ids, stream);
+  if (W <= 768) return launch_c<4, 3>(s, sel, W, g, ids, stream);
+  return launch_c<4, 4>(s, sel, W, g, ids, stream);
 }
 
 }  // namespace pw

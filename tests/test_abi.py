@@ -54,10 +54,10 @@ def test_group_validation():
     assert _group(_shape(), sel=None) == pw.PW_ERR_NULL
     assert _group(_shape(), ids=None) == pw.PW_ERR_NULL
     assert _group(_shape(), W=0) == pw.PW_ERR_UNSUPPORTED
-    assert _group(_shape(), W=257) == pw.PW_ERR_UNSUPPORTED
+    assert _group(_shape(), W=1025) == pw.PW_ERR_UNSUPPORTED
     assert _group(_shape(), g=17) == pw.PW_ERR_UNSUPPORTED
     assert _group(_shape(T=2048 * 16, N_pages=2048)) == pw.PW_ERR_UNSUPPORTED
-    assert b"W = 257" in (_group(_shape(), W=257) and pw._lib.pw_last_error())
+    assert b"W = 1025" in (_group(_shape(), W=1025) and pw._lib.pw_last_error())
     assert pw._lib.pw_group_workspace_bytes(ctypes.byref(_shape()), 32, 8) == 0
 
 

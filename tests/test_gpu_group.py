@@ -55,6 +55,38 @@ def test_group_windows_and_sizes(W, g):
     assert np.array_equal(got, ref)
 
 
+@pytest.mark.parametrize("W,g", [(384, 8), (512, 8), (768, 4), (1024, 8), (1000, 16), (300, 5),
+                                 (1024, 1), (640, 16)])
+def test_group_wide_windows(W, g):
+    # several waves share one window (W > 256); T = 2048 gives full and ragged windows
+    log(f"[case] pw_group wide window W={W} g={g}")
+    rng = np.random.default_rng(W * 7 + g)
+    T, P, S = 2048, 4, 12
+    N = T // P
+    sel = rng.integers(-3, N + 3, size=(2, T, S)).astype(np.int32)
+    sel[:, ::3] %= 20
+    sel[:, 1::5] = sel[:, 1::5] % 700      # words past 512 pages are never active: fewer words
+    got = _gpu_ids(sel, N, P, W, g)
+    ref = group_ids(sel, N, W, g, workers=WORKERS)
+    assert np.array_equal(got, ref), f"{(got != ref).sum()} IDs differ"
+
+
+def test_group_wide_window_64k_sample():
+    # W = 1024 at the 64K workload's shape; two windows per head against the oracle
+    wl = synth.WORKLOADS["prefill_64k"]
+    W, g = 1024, 8
+    log(f"[case] pw_group prefill_64k W={W} g={g} (sampled windows)")
+    sel = host_inputs("prefill_64k")["sel_pages"]
+    got = _gpu_ids(sel, wl.N, wl.P, W, g, wl.H_q, wl.D)
+    starts = {h: [0, (wl.T // W - 1) * W] if h % 2 == 0 else [(wl.T // W // 2) * W]
+              for h in range(wl.H_kv)}
+    ref = group_ids(sel, wl.N, W, g, workers=WORKERS, windows=starts)
+    for h, st in starts.items():
+        for w0 in st:
+            assert np.array_equal(got[h, w0:w0 + W], ref[h, w0:w0 + W]), (h, w0)
+    assert all(np.array_equal(np.sort(r), np.arange(wl.T)) for r in got)
+
+
 @pytest.mark.parametrize("N", [64, 100, 1024])
 def test_group_page_counts(N):
     log(f"[case] pw_group N={N}")
