@@ -8,47 +8,103 @@ uses the full membership of each page to form common and exclusive query lists
 union it produces one partial output per (query, page pair), so the per-query
 results have to be merged afterwards.
 
-Readings taken: pages are paired by ID as (2k, 2k+1); the full membership of a
-pair is every query of that KV head that selected either page; the common list
-holds the queries that selected both, the exclusive lists those that selected
-exactly one of them; each (query, Q head, pair) partial is (m, l, acc) over the
-query's own visible keys in the pair; partials are merged by log-sum-exp.  The
-merged result is the same O as ``oracle.attention`` (only the order of the
-floating-point work differs).
+Readings taken: pages are paired either by ID as (2k, 2k+1) or by affinity
+(below); the full membership of a pair is every query of that KV head that
+selected either page; the common list holds the queries that selected both, the
+exclusive lists those that selected exactly one of them; each (query, Q head,
+pair) partial is (m, l, acc) over the query's own visible keys in the pair;
+partials are merged by log-sum-exp.  The merged result is the same O as
+``oracle.attention`` for any partition of the pages into pairs (only the order
+of the floating-point work differs).
+
+Affinity pairs (the tuned variant of the design study): pages that many
+queries select together share more common-list entries, so pairs are chosen by
+co-selection.  co[u][v] counts the queries of the KV head whose support holds
+both u and v; the pairing is the greedy matching on the edges co > 0 taken in
+the order (larger count first, then lower first page, then lower second page):
+an edge joins the matching when both its pages are still free.  Unmatched
+pages stay single.  Pairs are numbered by their lower page.
+TEST INFRASTRUCTURE ONLY (see the package docstring).
 """
 from __future__ import annotations
 
 import math
-from typing import Dict, List
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
 from .attention import Problem
 
+Pair = Tuple[int, int]       # (lower page, higher page or -1 for a single page)
 
-def pair_lists(pb: Problem, h: int) -> Dict[int, Dict[str, List[int]]]:
-    """pair k -> {'common': [...], 'only_even': [...], 'only_odd': [...]}, sorted query IDs."""
+
+def adjacent_pairs(N: int) -> List[Pair]:
+    """Pairs (2k, 2k+1) by page ID; an odd last page stays single."""
+    return [(2 * k, 2 * k + 1 if 2 * k + 1 < N else -1) for k in range((N + 1) // 2)]
+
+
+def coselection(sel_h: np.ndarray, N: int) -> np.ndarray:
+    """co[u][v] = number of queries whose support (valid entries of its row) holds u and v;
+    the diagonal is 0.  int64 [N][N].  The count matrix is A^T A for the query x page
+    membership matrix A, formed with a float matmul (exact: counts are far below 2^24)."""
+    T = sel_h.shape[0]
+    A = np.zeros((T, N), dtype=np.float32)
+    rows, cols = np.nonzero((sel_h >= 0) & (sel_h < N))
+    A[rows, sel_h[rows, cols]] = 1.0
+    co = np.rint(A.T @ A).astype(np.int64)
+    np.fill_diagonal(co, 0)
+    return co
+
+
+def affinity_pairs(sel_h: np.ndarray, N: int) -> List[Pair]:
+    """Greedy co-selection matching of one KV head's pages, as described above."""
+    co = coselection(sel_h, N)
+    u, v = np.nonzero(np.triu(co, 1) > 0)
+    order = np.lexsort((v, u, -co[u, v]))          # count desc, then u, then v
+    mate = np.full(N, -1, dtype=np.int64)
+    for i in order:
+        a, b = int(u[i]), int(v[i])
+        if mate[a] < 0 and mate[b] < 0:
+            mate[a], mate[b] = b, a
+    return [(a, int(mate[a]) if mate[a] > a else -1) for a in range(N)
+            if mate[a] < 0 or mate[a] > a]
+
+
+def pair_lists(pb: Problem, h: int, pairs: Optional[Sequence[Pair]] = None
+               ) -> Dict[int, Dict[str, List[int]]]:
+    """pair k -> {'common': [...], 'only_first': [...], 'only_second': [...]}, sorted query IDs."""
+    pairs = adjacent_pairs(pb.N) if pairs is None else pairs
+    where = {}
+    for k, (a, b) in enumerate(pairs):
+        where[a] = (k, 0)
+        if b >= 0:
+            where[b] = (k, 1)
     lists: Dict[int, Dict[str, List[int]]] = {}
     for t in range(pb.T):
-        sup = set(pb.support(h, t).tolist())
-        for k in sorted({u // 2 for u in sup}):
-            has_e, has_o = (2 * k) in sup, (2 * k + 1) in sup
-            kind = "common" if (has_e and has_o) else ("only_even" if has_e else "only_odd")
-            lists.setdefault(k, {"common": [], "only_even": [], "only_odd": []})[kind].append(t)
+        hit: Dict[int, set] = {}
+        for u in pb.support(h, t).tolist():
+            k, pos = where[u]
+            hit.setdefault(k, set()).add(pos)
+        for k in sorted(hit):
+            kind = "common" if len(hit[k]) == 2 else ("only_first" if 0 in hit[k] else "only_second")
+            lists.setdefault(k, {"common": [], "only_first": [], "only_second": []})[kind].append(t)
     return lists
 
 
-def dense_union(pb: Problem) -> np.ndarray:
-    """O as fp64 [T][H_q][D] via per-pair partials and a log-sum-exp merge."""
+def dense_union(pb: Problem, pairing: Optional[Dict[int, Sequence[Pair]]] = None) -> np.ndarray:
+    """O as fp64 [T][H_q][D] via per-pair partials and a log-sum-exp merge.
+
+    ``pairing`` maps KV head -> its pairs (default: adjacent pairs for every head)."""
     G, D, P = pb.G, pb.D, pb.P
     out = np.zeros((pb.T, pb.H_q, D))
     for h in range(pb.H_kv):
+        pairs = adjacent_pairs(pb.N) if pairing is None else pairing[h]
         kh, vh = pb.k_hat(h), pb.v_hat(h)
         partials: Dict[int, list] = {}
-        for k, kinds in sorted(pair_lists(pb, h).items()):
+        for k, kinds in sorted(pair_lists(pb, h, pairs).items()):
+            a, b = pairs[k]
             for kind, members in kinds.items():
-                pages = {"common": [2 * k, 2 * k + 1], "only_even": [2 * k],
-                         "only_odd": [2 * k + 1]}[kind]
+                pages = {"common": [a, b], "only_first": [a], "only_second": [b]}[kind]
                 pos = (np.array(pages)[:, None] * P + np.arange(P)[None, :]).ravel()
                 kk = kh[pages].reshape(-1, D)
                 vv = vh[pages].reshape(-1, D)

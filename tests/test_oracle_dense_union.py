@@ -1,9 +1,19 @@
-"""Pins of the direct KV-page union oracle (CPU only)."""
+"""Pins of the direct KV-page union oracle (CPU only).
+
+The merged result is pinned to the per-query attention oracle for adjacent and
+affinity pairs.  The affinity matching is pinned by an independent brute force
+(co-selection counted with Python sets, the matching built by repeatedly taking
+the best remaining edge), by the certificate that characterises the greedy
+matching of a strict edge order (every unmatched edge has an endpoint matched
+by an earlier edge), and by a hand-worked case.
+"""
+import itertools
+
 import numpy as np
 import pytest
 
 from oracle.attention import Problem, attention
-from oracle.dense_union import dense_union, pair_lists
+from oracle.dense_union import adjacent_pairs, affinity_pairs, coselection, dense_union, pair_lists
 from tests.oracle_helpers import tiny_problem
 
 
@@ -30,10 +40,101 @@ def test_pair_lists_partition_membership():
                     sup = set(pb.support(h, t).tolist())
                     e, o = 2 * k in sup, 2 * k + 1 in sup
                     assert (kind == "common") == (e and o)
-                    assert (kind == "only_even") == (e and not o)
-                    assert (kind == "only_odd") == (o and not e)
+                    assert (kind == "only_first") == (e and not o)
+                    assert (kind == "only_second") == (o and not e)
         # every (query, selected page) lands in exactly one list of its pair
         for t in range(pb.T):
             for u in pb.support(h, t).tolist():
                 hits = [kind for kind, m in lists[u // 2].items() if t in m]
                 assert len(hits) == 1
+
+
+def _brute_pairs(sel_h, N):
+    """Independent brute force: set-based counts; repeatedly take the best free edge."""
+    sup = [set(int(u) for u in row if 0 <= u < N) for row in sel_h]
+    co = {}
+    for a, b in itertools.combinations(range(N), 2):
+        c = sum(1 for s in sup if a in s and b in s)
+        if c:
+            co[(a, b)] = c
+    free = set(range(N))
+    pairs = []
+    while True:
+        best = None
+        for (a, b), c in co.items():
+            if a in free and b in free:
+                if best is None or c > best[0] or (c == best[0] and (a, b) < best[1]):
+                    best = (c, (a, b))
+        if best is None:
+            break
+        a, b = best[1]
+        pairs.append((a, b))
+        free -= {a, b}
+    pairs += [(a, -1) for a in free]
+    return sorted(pairs)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_affinity_pairs_match_brute_force(seed):
+    rng = np.random.default_rng(seed)
+    T, N, S = 40, 12, 4
+    sel = rng.integers(-2, N + 1, size=(T, S)).astype(np.int32)
+    sel[::4] = sel[::4] % 3                       # repeated rows: many equal counts (ties)
+    assert affinity_pairs(sel, N) == _brute_pairs(sel, N)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_affinity_pairs_greedy_certificate(seed):
+    # a partition of the pages whose every unmatched edge (co > 0) has an endpoint
+    # matched by an edge earlier in the order is the greedy matching, and only it
+    inp = tiny_problem(T=512, P=8, Hq=2, Hkv=1, D=8, S=7, seed=seed)
+    sel, N = inp["sel_pages"][0], inp["k_codes"].shape[0]
+    pairs = affinity_pairs(sel, N)
+    co = coselection(sel, N)
+    pages = sorted([a for a, _ in pairs] + [b for _, b in pairs if b >= 0])
+    assert pages == list(range(N))                           # a partition
+    assert [a for a, _ in pairs] == sorted(a for a, _ in pairs)
+    mate = {}
+    for a, b in pairs:
+        assert b == -1 or (a < b and co[a, b] > 0)
+        if b >= 0:
+            mate[a], mate[b] = b, a
+    key = lambda a, b: (-co[a, b], min(a, b), max(a, b))
+    for a in range(N):
+        for b in range(a + 1, N):
+            if co[a, b] == 0 or mate.get(a) == b:
+                continue
+            dominated = any(x in mate and key(x, mate[x]) < key(a, b) for x in (a, b))
+            assert dominated, (a, b)
+    assert any(b >= 0 for _, b in pairs)
+
+
+def test_affinity_pairs_hand_case():
+    # pages 0..5; queries: four select {0, 1, 2}, three select {3, 4}, two select {2, 5}
+    # counts: (0,1)=4 (0,2)=4 (1,2)=4 (3,4)=3 (2,5)=2, all others 0.
+    # greedy: (0,1) first (count 4, lowest pages), then (0,2)/(1,2) are blocked,
+    # (3,4) next, then (2,5).  Every page is paired.
+    rows = [[0, 1, 2]] * 4 + [[3, 4, -1]] * 3 + [[2, 5, -1]] * 2
+    sel = np.array(rows, dtype=np.int32)
+    assert affinity_pairs(sel, 6) == [(0, 1), (2, 5), (3, 4)]
+    # a page nobody selects stays single; the count matrix ignores -1 and out-of-range IDs
+    sel2 = np.array([[0, 1, 7], [0, 1, -3]], dtype=np.int32)
+    assert affinity_pairs(sel2, 3) == [(0, 1), (2, -1)]
+    assert coselection(sel2, 3)[0, 1] == 2
+    co = coselection(sel, 6)
+    assert (np.diag(co) == 0).all() and (co == co.T).all()
+    assert co[0, 1] == co[0, 2] == co[1, 2] == 4 and co[3, 4] == 3 and co[2, 5] == 2 and co.sum() == 2 * 17
+
+
+def test_adjacent_pairs_shape():
+    assert adjacent_pairs(5) == [(0, 1), (2, 3), (4, -1)]
+    assert adjacent_pairs(4) == [(0, 1), (2, 3)]
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_affinity_partials_merge_to_the_per_query_result(seed):
+    inp = tiny_problem(T=256, P=8, Hq=4, Hkv=2, D=16, S=6, seed=seed)
+    pb = _pb(inp)
+    pairing = {h: affinity_pairs(inp["sel_pages"][h], pb.N) for h in range(pb.H_kv)}
+    assert any(b >= 0 and b != a + 1 for pr in pairing.values() for a, b in pr)   # not adjacent
+    np.testing.assert_allclose(dense_union(pb, pairing), attention(pb), rtol=0, atol=1e-12)
