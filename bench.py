@@ -66,6 +66,29 @@ def union_stats(sel: np.ndarray, ids: np.ndarray, g: int, N: int):
     return distinct.sum(axis=2)          # [H][ng]
 
 
+def pair_entries(sel: np.ndarray, pairs, N: int) -> float:
+    """Mean (query, page pair) entries per (KV head, query): adjacent pairs (2k, 2k+1) when
+    `pairs` is None, else the int32 [H_kv][N][2] pair table."""
+    H, T, S = sel.shape
+    valid = (sel >= 0) & (sel < N)
+    tot = 0
+    for h in range(H):
+        if pairs is None:
+            pid = np.arange(N) // 2
+        else:
+            pid = np.full(N, -1, dtype=np.int64)
+            for pos in (0, 1):
+                col = pairs[h, :, pos]
+                ok = col >= 0
+                pid[col[ok]] = np.nonzero(ok)[0]
+        k = np.where(valid[h], pid[np.clip(sel[h], 0, N - 1)], -1)
+        k = np.sort(k, axis=1)
+        distinct = k >= 0
+        distinct[:, 1:] &= k[:, 1:] != k[:, :-1]
+        tot += int(distinct.sum())
+    return tot / (H * T)
+
+
 def kernel_hash() -> str:
     src = os.path.join(ROOT, "query_union_paged_amd", "csrc", "union_attn.hip")
     return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
@@ -359,8 +382,30 @@ def main():
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / 2
         arms["direct_page_union"] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12,
-                                     "workspace_GiB": dws.numel() / 2 ** 30}
-        del dws
+                                     "workspace_GiB": dws.numel() / 2 ** 30,
+                                     "entries_per_query": pair_entries(inp["sel_pages"], None, wl.N)}
+        # the same with affinity pairs (greedy co-selection matching on the device)
+        pws = torch.empty(pw.pw_page_pairs_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
+        prs = pw.pw_page_pairs(shp, dev["sel_pages"], workspace=pws)
+        pw.pw_dense_union_ref(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
+                              dev["sel_pages"], O=O, workspace=dws, pairs=prs)
+        t = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        t[0].record(stream)
+        for _ in range(2):
+            pw.pw_page_pairs(shp, dev["sel_pages"], pairs=prs, workspace=pws)
+        t[1].record(stream)
+        for _ in range(2):
+            pw.pw_dense_union_ref(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
+                                  dev["sel_pages"], O=O, workspace=dws, pairs=prs)
+        t[2].record(stream)
+        torch.cuda.synchronize()
+        pair_ms, du_ms = t[0].elapsed_time(t[1]) / 2, t[1].elapsed_time(t[2]) / 2
+        arms["direct_page_union_affinity"] = {
+            "pairing_ms": pair_ms, "union_ms": du_ms, "ms": pair_ms + du_ms,
+            "useful_TFLOPs": F_u / ((pair_ms + du_ms) * 1e-3) / 1e12,
+            "entries_per_query": pair_entries(inp["sel_pages"], prs.cpu().numpy(), wl.N)}
+        log(f"[bench] direct page union: adjacent {ms:.2f} ms, affinity {pair_ms:.2f} + {du_ms:.2f} ms")
+        del dws, pws
         arms["selector"] = selector_arm(pw, torch, wl, dev, shp, O, ws)
 
     swp = sweep(pw, torch, wl, inp, dev, shp, O, ws) if args.sweep else None

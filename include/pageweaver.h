@@ -200,6 +200,53 @@ pw_status pw_dense_union_ref(const pw_shape* shape, const uint16_t* Q,
                              void* stream);
 
 /* ---------------------------------------------------------------------------
+ * pw_page_pairs -- affinity page pairs for the direct KV-page union.
+ *
+ * [abs]: the direct KV-page union weighs non-local reuse against the cost of
+ * reducing partial outputs; [radio "Paper summary"]: it works on disjoint page
+ * pairs with common and exclusive query lists.  Pairing pages that many
+ * queries select together moves entries to common lists and cuts the number
+ * of (query, pair) partials.
+ *
+ * Per KV head h: co[u][v] = number of queries t whose support (the valid
+ * entries of sel_pages[h][t]) holds both pages u != v.  The pairs are the
+ * greedy matching on the edges with co > 0 taken in the order (larger co,
+ * then lower first page, then lower second page): an edge is taken when both
+ * pages are still free.  Pages left free stay single.  The result is unique,
+ * so it is bit-exact against any correct implementation.
+ *
+ * In : sel_pages (see layouts).
+ * Out: pairs int32 [H_kv][N_pages][2] (device): row k = (a, b) with a < b, or
+ *      (a, -1) for a single page; rows are ordered by a and every page appears
+ *      exactly once; rows past the head's last pair are (-1, -1).
+ * Support set: N_pages <= 2048, T < 2^19.
+ * Workspace: pw_page_pairs_workspace_bytes(shape) bytes (page columns as
+ * query bitsets and the co-selection counts, H_kv * N_pages^2 * 4 bytes),
+ * 256-byte aligned.
+ * ------------------------------------------------------------------------- */
+size_t pw_page_pairs_workspace_bytes(const pw_shape* shape);
+pw_status pw_page_pairs(const pw_shape* shape, const int32_t* sel_pages, int32_t* pairs,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pw_dense_union_paired -- pw_dense_union_ref over a given page pairing.
+ *
+ * As pw_dense_union_ref, with pairs taken from `pairs` (int32 [H_kv][N_pages]
+ * [2], the layout pw_page_pairs writes) instead of (2k, 2k+1).  Each head's
+ * rows must partition its pages: every page 0..N_pages-1 in exactly one row,
+ * rows (-1, -1) ignored; a page in no row is treated as unselected and a page
+ * in two rows gives unspecified results.  Same O as pw_union_attention up to
+ * floating-point order, for any partition.
+ *
+ * Support set: as pw_dense_union_ref, with N_pages <= 2048.
+ * Workspace: pw_dense_union_ref_workspace_bytes(shape) bytes, 256-byte aligned.
+ * ------------------------------------------------------------------------- */
+pw_status pw_dense_union_paired(const pw_shape* shape, const uint16_t* Q, const uint8_t* K_fp8,
+                                const uint8_t* V_fp8, const float* scales,
+                                const int32_t* sel_pages, const int32_t* pairs, uint16_t* O,
+                                void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * pw_select -- a synthetic dynamic page selector producing sel_pages.
  *
  * [abs]: dynamic sparse attention gives every query its own set of selected

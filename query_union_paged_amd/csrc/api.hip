@@ -156,9 +156,54 @@ pw_status pw_dense_union_ref(const pw_shape* shape, const uint16_t* Q, const uin
   if (need > 0 && !ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
   if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   if (((uintptr_t)ws & 255) != 0) return fail(PW_ERR_DIMS, "workspace must be 256-byte aligned");
-  return hip_status(pw::launch_dense_union(*shape, Q, K_fp8, V_fp8, scales, sel_pages, O, ws,
-                                           ws_bytes, (hipStream_t)stream),
+  return hip_status(pw::launch_dense_union(*shape, Q, K_fp8, V_fp8, scales, sel_pages, nullptr, O,
+                                           ws, ws_bytes, (hipStream_t)stream),
                     "pw_dense_union_ref launch");
+}
+
+pw_status pw_dense_union_paired(const pw_shape* shape, const uint16_t* Q, const uint8_t* K_fp8,
+                                const uint8_t* V_fp8, const float* scales,
+                                const int32_t* sel_pages, const int32_t* pairs, uint16_t* O,
+                                void* ws, size_t ws_bytes, void* stream) {
+  pw_status st = check_shape(shape);
+  if (st != PW_OK) return st;
+  if (!Q || !K_fp8 || !V_fp8 || !scales || !sel_pages || !pairs || !O)
+    return fail(PW_ERR_NULL, "Q, K_fp8, V_fp8, scales, sel_pages, pairs and O are required");
+  st = check_attention_support(shape, 1);
+  if (st != PW_OK) return st;
+  if (shape->H_q / shape->H_kv > 8)
+    return fail(PW_ERR_UNSUPPORTED, "G = %d exceeds 8 for the page-pair tiles", shape->H_q / shape->H_kv);
+  if (shape->N_pages > 2048)
+    return fail(PW_ERR_UNSUPPORTED, "N_pages = %d exceeds 2048 for a pair table", shape->N_pages);
+  const size_t need = pw::dense_union_workspace(*shape);
+  if (!ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
+  if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (((uintptr_t)ws & 255) != 0) return fail(PW_ERR_DIMS, "workspace must be 256-byte aligned");
+  return hip_status(pw::launch_dense_union(*shape, Q, K_fp8, V_fp8, scales, sel_pages, pairs, O,
+                                           ws, ws_bytes, (hipStream_t)stream),
+                    "pw_dense_union_paired launch");
+}
+
+size_t pw_page_pairs_workspace_bytes(const pw_shape* shape) {
+  if (check_shape(shape) != PW_OK) return 0;
+  return pw::page_pairs_workspace(*shape);
+}
+
+pw_status pw_page_pairs(const pw_shape* shape, const int32_t* sel_pages, int32_t* pairs,
+                        void* ws, size_t ws_bytes, void* stream) {
+  pw_status st = check_shape(shape);
+  if (st != PW_OK) return st;
+  if (!sel_pages || !pairs) return fail(PW_ERR_NULL, "sel_pages and pairs are required");
+  if (shape->N_pages > 2048)
+    return fail(PW_ERR_UNSUPPORTED, "N_pages = %d exceeds 2048 for the pairing", shape->N_pages);
+  if (shape->T >= (1 << 19))
+    return fail(PW_ERR_UNSUPPORTED, "T = %d exceeds the co-selection count range", shape->T);
+  const size_t need = pw::page_pairs_workspace(*shape);
+  if (!ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
+  if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (((uintptr_t)ws & 255) != 0) return fail(PW_ERR_DIMS, "workspace must be 256-byte aligned");
+  return hip_status(pw::launch_page_pairs(*shape, sel_pages, pairs, ws, (hipStream_t)stream),
+                    "pw_page_pairs launch");
 }
 
 size_t pw_select_workspace_bytes(const pw_shape* shape) {

@@ -6,17 +6,23 @@
 // summary": it works on disjoint page pairs and uses the full membership of
 // each page to form common or exclusive query lists.
 //
-// The FP8 pages are first re-tiled in MFMA operand order (as for the query
-// union).  Then per chunk of Tc queries (all KV heads), on the caller's stream:
+// Pairs are either adjacent page IDs (2k, 2k + 1) or a caller-given table that
+// partitions the pages (e.g. the affinity matching of pair_match.hip); a page
+// map sends page u to slot 2k + (0 | 1) of its pair.  The FP8 pages are first
+// re-tiled in MFMA operand order (as for the query union).  Then per chunk of
+// Tc queries (all KV heads), on the caller's stream:
 //   1. zero the per-pair list lengths;
-//   2. pair_entries_kernel: one thread per (KV head, query) sets its page
-//      bitset in LDS, walks its pairs (2k, 2k+1) in ascending order and appends
+//   2. pair_entries_kernel: one thread per (KV head, query) sets its pair-slot
+//      bitset in LDS, walks its pairs in ascending order and appends
 //      (query, partial slot, which pages) to pair k's list -- the pair's full
 //      membership; an entry with both pages is on the common list, one page
 //      on an exclusive list; list ranges are reserved once per (wave, pair);
-//   3. pair attention (union_attn.hip, pair mode): tiles of 8 entries of a
+//   3. tile_scan_kernel: per KV head, the lists cut into tiles of 8 entries are
+//      numbered consecutively (an exclusive scan over the pairs), so the
+//      attention grid covers at most entries / 8 + pairs tiles per head;
+//   4. pair attention (union_attn.hip, pair mode): tiles of 8 entries of a
 //      list compute (m, l, acc) over their own visible keys of the pair;
-//   4. merge_kernel: one wave per (KV head, query) combines its partials by
+//   5. merge_kernel: one wave per (KV head, query) combines its partials by
 //      log-sum-exp into O (maximum first, then independent weighted loads).
 // The list order within a pair depends on atomics, but every partial has a
 // fixed slot and a row's arithmetic does not depend on the other rows of its
@@ -29,8 +35,8 @@ namespace {
 constexpr size_t kBudget = size_t(4) << 30;   // workspace bound (bytes)
 
 struct DUPlan {
-  int Np, maxp, Tc, NW;
-  size_t off_tiles, off_count, off_npairs, off_list, off_part, total;
+  int Np, maxp, Tc, NW;   // Np: pair capacity per head (N: any partition fits)
+  size_t off_tiles, off_count, off_tstart, off_pmap, off_npairs, off_list, off_part, total;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -38,9 +44,9 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 DUPlan plan(const pw_shape& s) {
   DUPlan d;
   const int G = s.H_q / s.H_kv;
-  d.Np = (s.N_pages + 1) / 2;
+  d.Np = s.N_pages;
   d.maxp = s.S < d.Np ? s.S : d.Np;
-  d.NW = (s.N_pages + 31) / 32;
+  d.NW = (2 * d.Np + 31) / 32;      // words of a query's pair-slot bitset
   const size_t per_token = (size_t)s.H_kv * ((size_t)d.maxp * G * (s.D + 4) * 4 + (size_t)d.Np * 8 + 4);
   size_t tc = kBudget / per_token;
   tc = tc / 64 * 64;
@@ -50,23 +56,72 @@ DUPlan plan(const pw_shape& s) {
   d.Tc = (int)tc;
   d.off_tiles = 0;
   d.off_count = align256(tiled_kv_bytes(s));
-  d.off_npairs = d.off_count + align256((size_t)s.H_kv * d.Np * 4);
+  d.off_tstart = d.off_count + align256((size_t)s.H_kv * d.Np * 4);
+  d.off_pmap = d.off_tstart + align256((size_t)s.H_kv * (d.Np + 1) * 4);
+  d.off_npairs = d.off_pmap + align256((size_t)s.H_kv * s.N_pages * 4);
   d.off_list = d.off_npairs + align256((size_t)s.H_kv * d.Tc * 4);
   d.off_part = d.off_list + align256((size_t)s.H_kv * d.Np * d.Tc * 8);
   d.total = d.off_part + align256((size_t)s.H_kv * d.Tc * d.maxp * G * (s.D + 4) * 4);
   return d;
 }
 
-__global__ void zero_kernel(int* p, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0;
+__global__ void fill_kernel(int* p, int n, int v) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = v;
 }
 
-// One wave per 64 queries of one KV head.  Each lane sets its query's page bitset
-// in LDS and walks its pairs (2k, 2k+1) in ascending order.  The wave first
+// pmap[h][u] = 2k + position of page u in pair k of the table (pmap starts at -1:
+// pages in no pair stay -1).  One thread per table row; rows (-1, -1) end it.
+__global__ void pair_map_kernel(const int2* __restrict__ pairs, int N, int Hkv, int* pmap) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= Hkv * N) return;
+  const int h = i / N, k = i - h * N;
+  const int2 pr = pairs[i];
+  if (pr.x >= 0 && pr.x < N) pmap[h * N + pr.x] = 2 * k;
+  if (pr.y >= 0 && pr.y < N) pmap[h * N + pr.y] = 2 * k + 1;
+}
+
+// Per KV head: tstart[k] = tiles (8 entries each) of pairs 0..k-1 and
+// tstart[Np] = all of the head's tiles.  One 1024-thread block per head; wave
+// scans by shuffles, wave totals through LDS.
+__global__ __launch_bounds__(1024) void tile_scan_kernel(const int* __restrict__ pcount, int Np,
+                                                         int* __restrict__ tstart) {
+  __shared__ int wsum[16];
+  const int h = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int* pc = pcount + (size_t)h * Np;
+  int* ts = tstart + (size_t)h * (Np + 1);
+  int running = 0;
+  for (int base = 0; base < Np; base += 1024) {
+    const int k = base + tid;
+    const int n = k < Np ? (pc[k] + 7) >> 3 : 0;
+    int x = n;                                     // inclusive scan within the wave
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wv] = x;
+    __syncthreads();
+    int woff = 0, all = 0;
+    for (int v = 0; v < 16; ++v) {
+      const int c = wsum[v];
+      woff += v < wv ? c : 0;
+      all += c;
+    }
+    if (k < Np) ts[k] = running + woff + x - n;
+    running += all;
+    __syncthreads();                               // wsum is rewritten next round
+  }
+  if (tid == 0) ts[Np] = running;
+}
+
+// One wave per 64 queries of one KV head.  Each lane sets its query's pair-slot
+// bitset in LDS (bit 2k + position for each selected page) and walks its pairs
+// in ascending order.  The wave first
 // counts its entries per pair in LDS, reserves one range per pair in the global
 // list (one atomic per (wave, pair) instead of one per entry: the sink and
 // local pairs are in every query's support), then writes its entries there.
-__global__ __launch_bounds__(64) void pair_entries_kernel(const int32_t* __restrict__ sel, int T,
+__global__ __launch_bounds__(64) void pair_entries_kernel(const int32_t* __restrict__ sel,
+                                                         const int* __restrict__ pmap, int T,
                                                          int S, int N, int NW, int Np, int Tc,
                                                          int maxp, int t0, int* pcount,
                                                          int* npairs, int2* plist) {
@@ -82,9 +137,13 @@ __global__ __launch_bounds__(64) void pair_entries_kernel(const int32_t* __restr
   const bool ok = tl < Tc && t < T;
   if (ok) {
     const int32_t* row = sel + ((size_t)h * T + t) * S;
+    const int* pm = pmap != nullptr ? pmap + (size_t)h * N : nullptr;
     for (int s2 = 0; s2 < S; ++s2) {
       const int u = row[s2];
-      if (u >= 0 && u < N) w[u >> 5] |= 1u << (u & 31);
+      if (u >= 0 && u < N) {
+        const int v = pm != nullptr ? pm[u] : u;   // adjacent pairs: slot = page
+        if (v >= 0) w[v >> 5] |= 1u << (v & 31);
+      }
     }
   }
   wave_sync();
@@ -96,7 +155,7 @@ __global__ __launch_bounds__(64) void pair_entries_kernel(const int32_t* __restr
       while (pm) {
         const int bit = __builtin_ctz(pm);
         pm &= pm - 1;
-        f(i * 16 + (bit >> 1), (int)((x >> bit) & 3));   // kind 1: page 2k, 2: 2k+1, 3: both
+        f(i * 16 + (bit >> 1), (int)((x >> bit) & 3));   // kind 1: first page, 2: second, 3: both
       }
     }
   };
@@ -182,11 +241,19 @@ size_t dense_union_workspace(const pw_shape& s) { return plan(s).total; }
 
 hipError_t launch_dense_union(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
                               const uint8_t* V, const float* scales, const int32_t* sel,
-                              uint16_t* O, void* ws, size_t ws_bytes, hipStream_t stream) {
+                              const int32_t* pairs, uint16_t* O, void* ws, size_t ws_bytes,
+                              hipStream_t stream) {
   const DUPlan d = plan(s);
   if (ws_bytes < d.total) return hipErrorInvalidValue;
   char* base = static_cast<char*>(ws);
   int* pcount = reinterpret_cast<int*>(base + d.off_count);
+  int* tstart = reinterpret_cast<int*>(base + d.off_tstart);
+  int* pmap = nullptr;
+  const int2* ptab = reinterpret_cast<const int2*>(pairs);
+  // pairs in use per head: adjacent IDs need ceil(N / 2); a table may use up to N
+  const int Np = pairs != nullptr ? d.Np : (s.N_pages + 1) / 2;
+  const int NW = (2 * Np + 31) / 32;
+  const int maxp = s.S < Np ? s.S : Np;
   int* npairs = reinterpret_cast<int*>(base + d.off_npairs);
   int2* plist = reinterpret_cast<int2*>(base + d.off_list);
   float* partials = reinterpret_cast<float*>(base + d.off_part);
@@ -194,25 +261,36 @@ hipError_t launch_dense_union(const pw_shape& s, const uint16_t* Q, const uint8_
   uint8_t* tiles = reinterpret_cast<uint8_t*>(base + d.off_tiles);
   hipError_t e0 = tile_kv(s, K, V, tiles, stream);
   if (e0 != hipSuccess) return e0;
+  const int n_map = s.H_kv * s.N_pages;
+  if (pairs != nullptr) {
+    pmap = reinterpret_cast<int*>(base + d.off_pmap);
+    hipLaunchKernelGGL(fill_kernel, dim3((n_map + 255) / 256), dim3(256), 0, stream, pmap, n_map,
+                       -1);
+    hipLaunchKernelGGL(pair_map_kernel, dim3((n_map + 255) / 256), dim3(256), 0, stream, ptab,
+                       s.N_pages, s.H_kv, pmap);
+  }
+  // tile slots per head: at most entries / 8 + one partial tile per pair
+  const int tiles_head = (int)(((size_t)d.Tc * maxp + 7) / 8) + Np;
   for (int t0 = 0; t0 < s.T; t0 += d.Tc) {
-    const int n_count = s.H_kv * d.Np;
-    hipLaunchKernelGGL(zero_kernel, dim3((n_count + 255) / 256), dim3(256), 0, stream, pcount,
-                       n_count);
+    const int n_count = s.H_kv * Np;
+    hipLaunchKernelGGL(fill_kernel, dim3((n_count + 255) / 256), dim3(256), 0, stream, pcount,
+                       n_count, 0);
     const int tcur = (s.T - t0 < d.Tc) ? s.T - t0 : d.Tc;
     hipLaunchKernelGGL(pair_entries_kernel, dim3((tcur + 63) / 64, s.H_kv), dim3(64),
-                       ((size_t)64 * (d.NW + 1) + 2 * (size_t)d.Np) * 4, stream, sel, s.T, s.S,
-                       s.N_pages, d.NW, d.Np,
-                       d.Tc, d.maxp, t0, pcount, npairs, plist);
+                       ((size_t)64 * (NW + 1) + 2 * (size_t)Np) * 4, stream, sel, pmap, s.T, s.S,
+                       s.N_pages, NW, Np, d.Tc, maxp, t0, pcount, npairs, plist);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    e = launch_pair_attention(s, Q, tiles, scales, plist, pcount, partials, d.Np, d.Tc, t0, stream);
+    hipLaunchKernelGGL(tile_scan_kernel, dim3(s.H_kv), dim3(1024), 0, stream, pcount, Np, tstart);
+    e = launch_pair_attention(s, Q, tiles, scales, plist, pcount, tstart, ptab, tiles_head,
+                              partials, Np, d.Tc, t0, stream);
     if (e != hipSuccess) return e;
     if (s.D == 128)
       hipLaunchKernelGGL(merge_kernel<128>, dim3(tcur, s.H_kv), dim3(64), 0, stream, partials,
-                         npairs, O, s.T, s.H_q, G, d.Tc, d.maxp, t0);
+                         npairs, O, s.T, s.H_q, G, d.Tc, maxp, t0);
     else
       hipLaunchKernelGGL(merge_kernel<64>, dim3(tcur, s.H_kv), dim3(64), 0, stream, partials,
-                         npairs, O, s.T, s.H_q, G, d.Tc, d.maxp, t0);
+                         npairs, O, s.T, s.H_q, G, d.Tc, maxp, t0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -51,6 +51,7 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
                                   hipStream_t stream);
 hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* tiles,
                                  const float* scales, const int2* plist, const int* pcount,
+                                 const int* tstart, const int2* pairs, int tiles_head,
                                  float* partials, int Np, int Tc, int t0, hipStream_t stream);
 size_t check_ids_workspace(const pw_shape& s);
 hipError_t launch_check_ids(const pw_shape& s, const int32_t* ids, int32_t* bad, void* ws,
@@ -59,8 +60,13 @@ size_t select_workspace(const pw_shape& s);
 hipError_t launch_select(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
                          const float* scales, int L, int32_t* sel, void* ws, hipStream_t stream);
 size_t dense_union_workspace(const pw_shape& s);
+// pairs: null = adjacent pages (2k, 2k + 1); else int32 [H_kv][N][2] pair table
 hipError_t launch_dense_union(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
                               const uint8_t* V, const float* scales, const int32_t* sel,
-                              uint16_t* O, void* ws, size_t ws_bytes, hipStream_t stream);
+                              const int32_t* pairs, uint16_t* O, void* ws, size_t ws_bytes,
+                              hipStream_t stream);
+size_t page_pairs_workspace(const pw_shape& s);
+hipError_t launch_page_pairs(const pw_shape& s, const int32_t* sel, int32_t* pairs, void* ws,
+                             hipStream_t stream);
 
 }  // namespace pw

@@ -62,8 +62,11 @@ struct UAParams {
   // page-pair mode (direct KV-page union): per (KV head, pair) entry lists
   const int2* plist;   // [H_kv][Np][Tc] (token - t0, partial slot | pages << 30)
   const int* pcount;   // [H_kv][Np] entries per list
+  const int* tstart;   // [H_kv][Np + 1] first tile of each pair's list; [Np] = tiles of the head
+  const int2* pairs;   // [H_kv][Np] the pair's pages (lower first, second -1 if single);
+                       // null: pair k is pages (2k, 2k + 1)
   float* partials;     // [slot][G][D + 4]: m, l, -, -, acc[D]
-  int Np, Tc, t0, tiles_per_pair;
+  int Np, Tc, t0, tiles_head;
 };
 
 enum : int { kUnionMode = 0, kPairMode = 1 };
@@ -237,25 +240,41 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   }
   wave_sync();
   } else {
-  // entries [8 * tile, 8 * tile + 8) of the list of pair k of KV head h
-  const int tile = gid % p.tiles_per_pair;
-  const int hk = gid / p.tiles_per_pair;
-  h = hk / p.Np;
-  const int k = hk - h * p.Np;
+  // Tile slot j of KV head h: the pairs' lists are cut into tiles of 8 entries,
+  // numbered consecutively over the pairs (tstart); slots past the head's
+  // last tile exit.  Pair k is the one with tstart[k] <= j < tstart[k + 1].
+  const int j = gid % p.tiles_head;
+  h = gid / p.tiles_head;
+  const int* ts = p.tstart + (size_t)h * (p.Np + 1);
+  if (j >= __builtin_amdgcn_readfirstlane(ts[p.Np])) return;
+  int lo = 0, hi = p.Np;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (__builtin_amdgcn_readfirstlane(ts[mid]) <= j) lo = mid; else hi = mid;
+  }
+  const int k = lo;
+  const int tile = j - __builtin_amdgcn_readfirstlane(ts[k]);
+  const int hk = h * p.Np + k;
   const int cnt = p.pcount[hk];
   gm = min(8, cnt - 8 * tile);
   if (gm <= 0) return;
+  int pa = 2 * k, pb = 2 * k + 1;
+  if (p.pairs != nullptr) {
+    const int2 pr = p.pairs[hk];
+    pa = __builtin_amdgcn_readfirstlane(pr.x);
+    pb = __builtin_amdgcn_readfirstlane(pr.y);
+  }
   int kind = 0;
   if (lane < gm) {
     const int2 e = p.plist[(size_t)hk * p.Tc + 8 * tile + lane];
     my_t = p.t0 + e.x;
     my_slot = e.y & 0x3FFFFFFF;
-    kind = (e.y >> 30) & 3;                 // bit 0: page 2k selected, bit 1: page 2k+1
+    kind = (e.y >> 30) & 3;                 // bit 0: the pair's first page selected, bit 1: second
   }
   const uint32_t m0 = (uint32_t)__ballot(kind & 1) & 0xFFu;
   const uint32_t m1 = (uint32_t)__ballot(kind & 2) & 0xFFu;
-  if (m0) list[n_u++] = (uint32_t)(2 * k) | (m0 << 16);
-  if (m1) list[n_u++] = (uint32_t)(2 * k + 1) | (m1 << 16);
+  if (m0) list[n_u++] = (uint32_t)pa | (m0 << 16);
+  if (m1) list[n_u++] = (uint32_t)pb | (m1 << 16);
   wave_sync();
   }
   const int tmin = __builtin_amdgcn_readfirstlane(
@@ -619,17 +638,18 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
 
 hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* tiles,
                                  const float* scales, const int2* plist, const int* pcount,
+                                 const int* tstart, const int2* pairs, int tiles_head,
                                  float* partials, int Np, int Tc, int t0, hipStream_t stream) {
   UAParams prm;
   common_params(prm, s, Q, scales);
   prm.Kt = tiles;
   prm.Vt = tiles + tiled_kv_bytes(s) / 2;
   prm.plist = plist; prm.pcount = pcount; prm.partials = partials;
+  prm.tstart = tstart; prm.pairs = pairs; prm.tiles_head = tiles_head;
   prm.Np = Np; prm.Tc = Tc; prm.t0 = t0;
   prm.g = 8;
-  prm.tiles_per_pair = (Tc + 7) / 8;
   prm.n_rt = (8 * prm.G + 31) / 32;
-  prm.total_items = s.H_kv * Np * prm.tiles_per_pair * prm.n_rt;
+  prm.total_items = s.H_kv * tiles_head * prm.n_rt;
   prm.n_umax = 2;
   prm.lds_wave = 16;
   const int blocks = (prm.total_items + PW_UA_WG_WAVES - 1) / PW_UA_WG_WAVES;

@@ -54,6 +54,9 @@ _SIGS = {
     "pw_select": (_i32, [_SHP, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "pw_dense_union_ref_workspace_bytes": (_sz, [_SHP]),
     "pw_dense_union_ref": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pw_dense_union_paired": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pw_page_pairs_workspace_bytes": (_sz, [_SHP]),
+    "pw_page_pairs": (_i32, [_SHP, _vp, _vp, _vp, _sz, _vp]),
     "pw_status_string": (ctypes.c_char_p, [_i32]),
     "pw_last_error": (ctypes.c_char_p, []),
     "pw_abi_version": (_i32, []),
@@ -182,7 +185,9 @@ def pw_dense_union_ref_workspace_bytes(shp: PWShape) -> int:
 
 def pw_dense_union_ref(shp: PWShape, Q, K_fp8, V_fp8, scales, sel_pages,
                        O: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                       stream=None) -> torch.Tensor:
+                       stream=None, pairs: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Direct KV-page union; adjacent pairs (2k, 2k+1), or `pairs` (int32 [H_kv][N][2], e.g.
+    from pw_page_pairs) through pw_dense_union_paired."""
     T, Hq, Hkv, D, P, N, S = shp.T, shp.H_q, shp.H_kv, shp.D, shp.P, shp.N_pages, shp.S
     q = _dev(Q, "Q", _BF16, (T, Hq, D))
     k = _dev(K_fp8, "K_fp8", _U8, (N, Hkv, P, D))
@@ -196,9 +201,34 @@ def pw_dense_union_ref(shp: PWShape, Q, K_fp8, V_fp8, scales, sel_pages,
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=Q.device)
     ws, nbytes = (0, 0) if workspace is None else (_dev(workspace, "workspace", (torch.uint8,)), workspace.numel())
-    _check(_lib.pw_dense_union_ref(ctypes.byref(shp), q, k, v, sc, sel, o, ws or None, nbytes,
-                                   _stream(stream)), "pw_dense_union_ref")
+    if pairs is None:
+        _check(_lib.pw_dense_union_ref(ctypes.byref(shp), q, k, v, sc, sel, o, ws or None, nbytes,
+                                       _stream(stream)), "pw_dense_union_ref")
+    else:
+        pr = _dev(pairs, "pairs", (torch.int32,), (Hkv, N, 2))
+        _check(_lib.pw_dense_union_paired(ctypes.byref(shp), q, k, v, sc, sel, pr, o, ws or None,
+                                          nbytes, _stream(stream)), "pw_dense_union_paired")
     return O
+
+
+def pw_page_pairs_workspace_bytes(shp: PWShape) -> int:
+    return int(_lib.pw_page_pairs_workspace_bytes(ctypes.byref(shp)))
+
+
+def pw_page_pairs(shp: PWShape, sel_pages, pairs: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Affinity page pairs (greedy co-selection matching): int32 [H_kv][N_pages][2]."""
+    sel = _dev(sel_pages, "sel_pages", (torch.int32,), (shp.H_kv, shp.T, shp.S))
+    if pairs is None:
+        pairs = torch.empty((shp.H_kv, shp.N_pages, 2), dtype=torch.int32, device=sel_pages.device)
+    pr = _dev(pairs, "pairs", (torch.int32,), (shp.H_kv, shp.N_pages, 2))
+    if workspace is None:
+        workspace = torch.empty(pw_page_pairs_workspace_bytes(shp), dtype=torch.uint8,
+                                device=sel_pages.device)
+    ws = _dev(workspace, "workspace", (torch.uint8,))
+    _check(_lib.pw_page_pairs(ctypes.byref(shp), sel, pr, ws, workspace.numel(), _stream(stream)),
+           "pw_page_pairs")
+    return pairs
 
 
 def to_device(inputs: dict, device="cuda") -> dict:

@@ -94,6 +94,25 @@ def test_dense_union_validation():
         assert f(ctypes.byref(shp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, need, None) == pw.PW_ERR_NULL
 
 
+def test_page_pairs_validation():
+    f = pw._lib.pw_page_pairs
+    shp = _shape()
+    need = pw._lib.pw_page_pairs_workspace_bytes(ctypes.byref(shp))
+    assert need >= shp.H_kv * shp.N_pages * shp.N_pages * 4       # the co-selection counts
+    assert f(ctypes.byref(shp), None, FAKE, FAKE, need, None) == pw.PW_ERR_NULL
+    assert f(ctypes.byref(shp), FAKE, None, FAKE, need, None) == pw.PW_ERR_NULL
+    assert f(ctypes.byref(shp), FAKE, FAKE, None, need, None) == pw.PW_ERR_NULL
+    assert f(ctypes.byref(shp), FAKE, FAKE, FAKE, need - 1, None) == pw.PW_ERR_WORKSPACE
+    assert f(ctypes.byref(shp), FAKE, FAKE, ctypes.c_void_p(0x1010), need, None) == pw.PW_ERR_DIMS
+    big = _shape(T=4096 * 16, N_pages=4096)
+    assert f(ctypes.byref(big), FAKE, FAKE, FAKE, 1 << 40, None) == pw.PW_ERR_UNSUPPORTED
+    g = pw._lib.pw_dense_union_paired
+    need = pw._lib.pw_dense_union_ref_workspace_bytes(ctypes.byref(shp))
+    assert g(ctypes.byref(shp), *[FAKE] * 5, None, FAKE, FAKE, need, None) == pw.PW_ERR_NULL
+    assert g(ctypes.byref(shp), *[FAKE] * 7, FAKE, need - 1, None) == pw.PW_ERR_WORKSPACE
+    assert g(ctypes.byref(big), *[FAKE] * 7, FAKE, 1 << 40, None) == pw.PW_ERR_UNSUPPORTED
+
+
 def test_select_validation():
     f = pw._lib.pw_select
     shp = _shape(S=8)
