@@ -198,6 +198,8 @@ pw_status pw_page_pairs(const pw_shape* shape, const int32_t* sel_pages, int32_t
     return fail(PW_ERR_UNSUPPORTED, "N_pages = %d exceeds 2048 for the pairing", shape->N_pages);
   if (shape->T >= (1 << 19))
     return fail(PW_ERR_UNSUPPORTED, "T = %d exceeds the co-selection count range", shape->T);
+  if ((size_t)shape->H_kv * shape->N_pages * shape->N_pages >= ((size_t)1 << 31))
+    return fail(PW_ERR_UNSUPPORTED, "H_kv * N_pages^2 co-selection counts exceed 2^31");
   const size_t need = pw::page_pairs_workspace(*shape);
   if (!ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
   if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);

@@ -293,15 +293,15 @@ __global__ __launch_bounds__(1024) void match_kernel(const int* __restrict__ co,
       const int u = __builtin_amdgcn_readfirstlane(todo[i]);
       uint32_t kb = 0;
       const int* row = C + (size_t)u * N;
-      for (int v0 = 0; v0 < N; v0 += 64 * 8) {      // 8 loads in flight per lane
-        int c[8];
+      for (int v0 = 0; v0 < N; v0 += 64 * 16) {     // 16 loads in flight per lane
+        int c[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 16; ++j) {
           const int v = v0 + 64 * j + lane;
           c[j] = v < N ? row[v] : 0;
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 16; ++j) {
           const int v = v0 + 64 * j + lane;
           if (c[j] > 0 && mate[v] == -1) kb = max(kb, pair_key((uint32_t)c[j], v));
         }
