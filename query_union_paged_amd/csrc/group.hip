@@ -7,9 +7,11 @@
 // sets add few new pages; g is fixed independently of the window W.
 //
 // One wave per (KV head, aligned window).  Lane l owns candidates l, l+64,
-// l+128, ... (C = ceil(W/64) of them) and keeps their page bitsets in VGPRs,
-// compacted to the words the window uses; the bitsets are built 64
-// candidates at a time in LDS from 16-byte loads of the selection rows.  A
+// l+128, ... (C = ceil(W/64) of them) and keeps their page bitsets in VGPRs
+// over the window's pages only (page -> its rank among the distinct pages the
+// window selects, so the width is set by how many pages the window uses, not
+// by their spread); the bitsets are built 64 candidates at a time in LDS from
+// 16-byte loads of the selection rows.  A
 // step is a wave minimum of key = (cost << 10 | local index) over the
 // available candidates (DPP within rows of 16, then four readlanes), so the
 // lowest index wins ties and the result is bit-exact.  The winner's words
@@ -42,30 +44,24 @@ __device__ __forceinline__ uint32_t wave_min_dpp(uint32_t v) {
   return min(min(a, b), min(c, d));
 }
 
-__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
-  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
-  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, true);
-  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, true);
-  v |= (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, true);
-  return __builtin_amdgcn_readlane(v, 0) | __builtin_amdgcn_readlane(v, 16) |
-         __builtin_amdgcn_readlane(v, 32) | __builtin_amdgcn_readlane(v, 48);
-}
-
 // The greedy loop of one window.  The window's bitsets are staged 64
-// candidates at a time (LDS `stage`) and kept in registers compacted to the
-// window's active words (word jj = the jj-th word any candidate uses; words
-// past the active count are zero for every candidate and cost nothing).
-// With NWV > 1 waves per window (W > 256), wave wv owns candidates
-// 256 wv + 64 c + lane; each step then takes the minimum over the waves' minima
+// candidates at a time (LDS `stage`) and kept in registers over page ranks
+// (`rank`: a page's index among the window's distinct pages), NWB words wide;
+// words past the last rank are zero for every candidate and cost nothing.
+// With NWV > 1 waves per window, wave wv owns candidates
+// 64 C wv + 64 c + lane; each step then takes the minimum over the waves' minima
 // through LDS (`xch`), and the owner of the chosen candidate publishes its
 // words there (two workgroup barriers per step).
 template <int C, int NWB, int NWV>
 __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, int S, int N,
-                                            int Wr, int g, uint32_t act, uint32_t* stage,
-                                            int* order, uint32_t* xch) {
+                                            int Wr, int g, const uint16_t* rank,
+                                            uint32_t* stage, int* order, uint32_t* xch) {
   const int lane = threadIdx.x & 63;
   const int wv = NWV > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
-  const int cbase = 256 * wv;                // first candidate of this wave
+  static_assert(NWV == 1 || (C & (C - 1)) == 0, "several waves need C in {1, 2, 4}");
+  // candidate index -> owning wave (log2(64 C); one wave: always 0)
+  constexpr int kShift = NWV == 1 ? 16 : C == 4 ? 8 : C == 2 ? 7 : 6;
+  const int cbase = 64 * C * wv;             // first candidate of this wave
   uint32_t b[C][NWB];
   // one 64-candidate chunk: bits set in LDS, then each lane takes its row
   auto build_chunk = [&](uint32_t(&bc)[NWB], const int c) __attribute__((always_inline)) {
@@ -75,9 +71,10 @@ __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, i
     const int nrows = max(0, min(64, Wr - r0));
     const int32_t* base = wbase + (size_t)r0 * S;
     auto put = [&](int r, int u) __attribute__((always_inline)) {
-      if (u >= 0 && u < N)
-        atomicOr(&stage[r * kStride + __builtin_popcount(act & ((1u << (u >> 5)) - 1u))],
-                 1u << (u & 31));
+      if (u >= 0 && u < N) {
+        const int k = rank != nullptr ? rank[u] : u;   // the page's index among the window's pages
+        atomicOr(&stage[r * kStride + (k >> 5)], 1u << (k & 31));
+      }
     };
     if ((S & 3) == 0) {          // 16-byte loads, 8 per lane in flight
       const int n4 = (nrows * S) >> 2;
@@ -175,7 +172,7 @@ __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, i
     for (int c = 0; c < C; ++c)
       if ((avail >> c) & 1u) key = min(key, (uint32_t)(cbase + 64 * c + lane));
     uint32_t best = window_min(key);
-    int wb = best >> 8, cb = (best >> 6) & 3, lb = best & 63;
+    int wb = best >> kShift, cb = (best >> 6) - C * wb, lb = best & 63;
     if (wb == wv && lane == lb) avail &= ~(1u << cb);
     if (wv == 0 && lane == 0) order[pos] = (int)best;
     ++pos;
@@ -195,8 +192,8 @@ __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, i
         if ((avail >> c) & 1u)
           key = min(key, ((tot[c] - gain[c]) << 10) | (uint32_t)(cbase + 64 * c + lane));
       best = window_min(key) & 1023u;
-      wb = best >> 8;
-      cb = (best >> 6) & 3;
+      wb = best >> kShift;
+      cb = (best >> 6) - C * wb;
       lb = best & 63;
       if (wb == wv && lane == lb) avail &= ~(1u << cb);
       if (wv == 0 && lane == 0) order[pos] = (int)best;
@@ -225,16 +222,31 @@ __global__ __launch_bounds__(64 * NWV) void group_kernel(const int32_t* __restri
   const int wv = NWV > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   uint32_t* stage = lds + wv * 64 * kStride;                      // [64][kStride] per wave
   int* order = reinterpret_cast<int*>(lds + NWV * 64 * kStride);  // [NWV C 64] emission order
-  uint32_t* xch = lds + NWV * 64 * kStride + NWV * C * 64;        // [4 keys | 32 words | 4 act]
+  uint32_t* xch = lds + NWV * 64 * kStride + NWV * C * 64;        // [4 keys | 32 words]
+  uint32_t* apg = xch + 36;                                       // [32] the window's pages
+  int* wpre = reinterpret_cast<int*>(apg + 32);                   // [32] ranks before each word
+  uint16_t* rank = reinterpret_cast<uint16_t*>(wpre + 32);        // [N] page -> rank
   const int h = blockIdx.x / n_windows;
   const int w0 = (blockIdx.x % n_windows) * W;
   const int Wr = min(W, T - w0);
   const int32_t* wbase = sel + ((size_t)h * T + w0) * S;
   // this wave's candidate rows
-  const int r_lo = min(Wr, 256 * wv), r_hi = min(Wr, 256 * wv + 64 * C);
+  const int r_lo = min(Wr, 64 * C * wv), r_hi = min(Wr, 64 * C * (wv + 1));
 
-  // words (32 pages each) that some candidate of the window uses
-  uint32_t act = 0;
+  // the window's pages (bitset apg over N <= 1024 pages), then every page's rank
+  // among them: bitsets are kept over ranks, so their width follows the number
+  // of distinct pages in the window, not how widely those pages are spread
+  auto sync = [&]() __attribute__((always_inline)) {
+    if constexpr (NWV > 1) __syncthreads(); else wave_sync();
+  };
+  if (N <= 256) {            // every page fits in 8 words: pages are their own ranks
+    window_body<C, 8, NWV>(wbase, S, N, Wr, g, nullptr, stage, order, xch);
+    sync();
+    for (int i = threadIdx.x; i < Wr; i += 64 * NWV) ids[(size_t)h * T + w0 + i] = w0 + order[i];
+    return;
+  }
+  if (threadIdx.x < 32) apg[threadIdx.x] = 0;
+  sync();
   if ((S & 3) == 0) {
     const int lo4 = (r_lo * S) >> 2, n4 = (r_hi * S) >> 2;
     const int4* w4 = reinterpret_cast<const int4*>(wbase);
@@ -250,35 +262,37 @@ __global__ __launch_bounds__(64 * NWV) void group_kernel(const int32_t* __restri
         const int e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
 #pragma unroll
         for (int k = 0; k < 4; ++k)
-          if (e[k] >= 0 && e[k] < N) act |= 1u << (e[k] >> 5);
+          if (e[k] >= 0 && e[k] < N) atomicOr(&apg[e[k] >> 5], 1u << (e[k] & 31));
       }
     }
   } else {
     for (int i = r_lo * S + lane; i < r_hi * S; i += 64) {
       const int u = wbase[i];
-      if (u >= 0 && u < N) act |= 1u << (u >> 5);
+      if (u >= 0 && u < N) atomicOr(&apg[u >> 5], 1u << (u & 31));
     }
   }
-  act = wave_or(act);
-  if constexpr (NWV > 1) {
-    if (lane == 0) xch[36 + wv] = act;
-    __syncthreads();
-    act = 0;
+  sync();
+  // exclusive prefix of the words' page counts (lanes 0..31 of every wave)
+  const uint32_t aw = lane < 32 ? apg[lane] : 0u;
+  int x = __builtin_popcount(aw);
 #pragma unroll
-    for (int v = 0; v < NWV; ++v) act |= xch[36 + v];
-    act = __builtin_amdgcn_readfirstlane(act);
+  for (int d = 1; d < 32; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
   }
-  const int nact = __builtin_popcount(act);
-  if (nact <= 8)
-    window_body<C, 8, NWV>(wbase, S, N, Wr, g, act, stage, order, xch);
-  else if (nact <= 16)
-    window_body<C, 16, NWV>(wbase, S, N, Wr, g, act, stage, order, xch);
+  const int n_act = __builtin_amdgcn_readlane(x, 31);
+  if (wv == 0 && lane < 32) wpre[lane] = x - __builtin_popcount(aw);
+  sync();
+  for (int u = threadIdx.x; u < N; u += 64 * NWV)
+    rank[u] = (uint16_t)(wpre[u >> 5] + __builtin_popcount(apg[u >> 5] & ((1u << (u & 31)) - 1u)));
+  sync();
+  if (n_act <= 256)
+    window_body<C, 8, NWV>(wbase, S, N, Wr, g, rank, stage, order, xch);
+  else if (n_act <= 512)
+    window_body<C, 16, NWV>(wbase, S, N, Wr, g, rank, stage, order, xch);
   else
-    window_body<C, 32, NWV>(wbase, S, N, Wr, g, act, stage, order, xch);
-  if constexpr (NWV > 1)
-    __syncthreads();
-  else
-    wave_sync();
+    window_body<C, 32, NWV>(wbase, S, N, Wr, g, rank, stage, order, xch);
+  sync();
   for (int i = threadIdx.x; i < Wr; i += 64 * NWV) ids[(size_t)h * T + w0 + i] = w0 + order[i];
 }
 
@@ -286,7 +300,8 @@ template <int C, int NWV>
 hipError_t launch_c(const pw_shape& s, const int32_t* sel, int W, int g, int32_t* ids,
                     hipStream_t stream) {
   const int n_windows = (s.T + W - 1) / W;
-  const size_t lds = ((size_t)NWV * 64 * kStride + (size_t)NWV * C * 64 + 40) * 4;
+  const size_t lds =
+      ((size_t)NWV * 64 * kStride + (size_t)NWV * C * 64 + 36 + 32 + 32) * 4 + (size_t)s.N_pages * 2;
   hipLaunchKernelGGL((group_kernel<C, NWV>), dim3(s.H_kv * n_windows), dim3(64 * NWV), lds,
                      stream, sel, ids, s.T, s.S, s.N_pages, W, g, n_windows);
   return hipGetLastError();
