@@ -199,6 +199,32 @@ def sweep(pw, torch, wl, inp, dev, shp, O, ws, reps: int = 5):
     return rows
 
 
+def head_pipeline_arm(pw, torch, wl, dev, shp, O, ws, reps: int = 10):
+    """The complete call with the search of later KV heads overlapping the attention of
+    earlier ones (pw_group per head chunk on a second stream, pw_union_attention_heads per
+    chunk on the caller's stream after its search), for chunks of 1, 2 and 4 heads."""
+    stream = torch.cuda.current_stream()
+    ids = torch.empty((wl.H_kv, wl.T), dtype=torch.int32, device="cuda")
+    out = {}
+    for chunk in (1, 2, 4):
+        if wl.H_kv % chunk:
+            continue
+        run = pw.HeadPipeline(shp, chunk)
+        call = lambda: run(dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
+                           dev["sel_pages"], wl.W, wl.g, ids, O, ws)
+        for _ in range(2):
+            call()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        out[f"chunk{chunk}_ms"] = a.elapsed_time(b) / reps
+        log(f"[bench] head pipeline, {chunk} KV heads per chunk: {out[f'chunk{chunk}_ms']:.3f} ms")
+    return out
+
+
 def selector_arm(pw, torch, wl, dev, shp, O, ws, reps: int = 5):
     """The synthetic GPU selector (sink + 2 local pages + top pages by block key sums) and the
     complete call on its selections, regrouped and with identity grouping."""
@@ -407,6 +433,7 @@ def main():
         log(f"[bench] direct page union: adjacent {ms:.2f} ms, affinity {pair_ms:.2f} + {du_ms:.2f} ms")
         del dws, pws
         arms["selector"] = selector_arm(pw, torch, wl, dev, shp, O, ws)
+        arms["head_pipeline"] = head_pipeline_arm(pw, torch, wl, dev, shp, O, ws)
 
     swp = sweep(pw, torch, wl, inp, dev, shp, O, ws) if args.sweep else None
 

@@ -171,6 +171,30 @@ pw_status pw_union_attention(const pw_shape* shape, const uint16_t* Q,
                              void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * pw_union_attention_heads -- pw_union_attention for KV heads
+ * [h_begin, h_begin + h_count) only.
+ *
+ * [radio "Conclusion"]: the cost of a call includes building its groups; the
+ * search and the attention are independent per KV head, so a caller can run
+ * the search of later heads while earlier heads attend: pw_group on a head
+ * range (pass sel_pages and query_ids offset by h_begin rows and a shape with
+ * H_kv = h_count, H_q = G * h_count: both layouts are head-major), then this
+ * call for the same range on another stream once that search is done.
+ *
+ * Arguments as pw_union_attention (full shape, full tensors); only the rows of
+ * O of Q heads [h_begin * G, (h_begin + h_count) * G) are written, and only the
+ * range's heads of the workspace's re-tiled K/V copy.  Calls for disjoint head
+ * ranges may therefore share one workspace and run concurrently on different
+ * streams.  Out-of-range heads: PW_ERR_DIMS.
+ * ------------------------------------------------------------------------- */
+pw_status pw_union_attention_heads(const pw_shape* shape, const uint16_t* Q,
+                                   const uint8_t* K_fp8, const uint8_t* V_fp8,
+                                   const float* scales, const int32_t* sel_pages,
+                                   const int32_t* query_ids, int32_t g, int32_t h_begin,
+                                   int32_t h_count, uint16_t* O, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* ---------------------------------------------------------------------------
  * pw_dense_union_ref -- direct KV-page union (design-study comparison).
  *
  * [abs]: a direct KV-page union implementation studies non-local reuse

@@ -113,16 +113,21 @@ size_t pw_union_attention_workspace_bytes(const pw_shape* shape, int32_t) {
   return pw::tiled_kv_bytes(*shape);
 }
 
-pw_status pw_union_attention(const pw_shape* shape, const uint16_t* Q, const uint8_t* K_fp8,
-                             const uint8_t* V_fp8, const float* scales, const int32_t* sel_pages,
-                             const int32_t* query_ids, int32_t g, uint16_t* O, void* ws,
-                             size_t ws_bytes, void* stream) {
+static pw_status union_attention_range(const pw_shape* shape, const uint16_t* Q,
+                                       const uint8_t* K_fp8, const uint8_t* V_fp8,
+                                       const float* scales, const int32_t* sel_pages,
+                                       const int32_t* query_ids, int32_t g, int32_t h_begin,
+                                       int32_t h_count, uint16_t* O, void* ws, size_t ws_bytes,
+                                       void* stream, const char* what) {
   pw_status st = check_shape(shape);
   if (st != PW_OK) return st;
   if (!Q || !K_fp8 || !V_fp8 || !scales || !sel_pages || !query_ids || !O)
     return fail(PW_ERR_NULL, "Q, K_fp8, V_fp8, scales, sel_pages, query_ids and O are required");
   st = check_attention_support(shape, g);
   if (st != PW_OK) return st;
+  if (h_begin < 0 || h_count < 1 || h_begin + h_count > shape->H_kv)
+    return fail(PW_ERR_DIMS, "KV heads [%d, %d) outside [0, %d)", h_begin, h_begin + h_count,
+                shape->H_kv);
   const size_t need = pw::tiled_kv_bytes(*shape);
   if (!ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
   if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -130,8 +135,28 @@ pw_status pw_union_attention(const pw_shape* shape, const uint16_t* Q, const uin
   if (need / 2 > 0x7FFFFFFFu)
     return fail(PW_ERR_UNSUPPORTED, "tiled K/V of %zu bytes exceeds 2 GiB", need / 2);
   return hip_status(pw::launch_union_attention(*shape, Q, K_fp8, V_fp8, scales, sel_pages,
-                                               query_ids, g, O, ws, (hipStream_t)stream),
-                    "pw_union_attention launch");
+                                               query_ids, g, h_begin, h_count, O, ws,
+                                               (hipStream_t)stream),
+                    what);
+}
+
+pw_status pw_union_attention(const pw_shape* shape, const uint16_t* Q, const uint8_t* K_fp8,
+                             const uint8_t* V_fp8, const float* scales, const int32_t* sel_pages,
+                             const int32_t* query_ids, int32_t g, uint16_t* O, void* ws,
+                             size_t ws_bytes, void* stream) {
+  return union_attention_range(shape, Q, K_fp8, V_fp8, scales, sel_pages, query_ids, g, 0,
+                               shape ? shape->H_kv : 0, O, ws, ws_bytes, stream,
+                               "pw_union_attention launch");
+}
+
+pw_status pw_union_attention_heads(const pw_shape* shape, const uint16_t* Q,
+                                   const uint8_t* K_fp8, const uint8_t* V_fp8,
+                                   const float* scales, const int32_t* sel_pages,
+                                   const int32_t* query_ids, int32_t g, int32_t h_begin,
+                                   int32_t h_count, uint16_t* O, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  return union_attention_range(shape, Q, K_fp8, V_fp8, scales, sel_pages, query_ids, g, h_begin,
+                               h_count, O, ws, ws_bytes, stream, "pw_union_attention_heads launch");
 }
 
 size_t pw_dense_union_ref_workspace_bytes(const pw_shape* shape) {

@@ -43,12 +43,13 @@ hipError_t launch_group(const pw_shape& s, const int32_t* sel, int W, int g, int
                         hipStream_t stream);
 // FP8 K/V pages re-tiled in MFMA operand order (K tiles, then V tiles).
 size_t tiled_kv_bytes(const pw_shape& s);
+// KV heads h_begin .. h_begin + h_count - 1 (h_count < 0: all heads)
 hipError_t tile_kv(const pw_shape& s, const uint8_t* K, const uint8_t* V, uint8_t* tiles,
-                   hipStream_t stream);
+                   hipStream_t stream, int h_begin = 0, int h_count = -1);
 hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
                                   const uint8_t* V, const float* scales, const int32_t* sel,
-                                  const int32_t* ids, int g, uint16_t* O, void* ws,
-                                  hipStream_t stream);
+                                  const int32_t* ids, int g, int h_begin, int h_count,
+                                  uint16_t* O, void* ws, hipStream_t stream);
 hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* tiles,
                                  const float* scales, const int2* plist, const int* pcount,
                                  const int* tstart, const int2* pairs, int tiles_head,

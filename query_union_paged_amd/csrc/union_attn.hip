@@ -54,6 +54,7 @@ struct UAParams {
   uint16_t* O;
   int T, Hq, Hkv, G, P, N, S, g;
   int groups_per_head, total_groups;
+  int h_begin;       // first KV head of the call (groups cover heads h_begin ...)
   int n_rt;          // 32-row tiles per group (ceil(g * G / 32)): one wave each
   int total_items;   // total_groups * n_rt
   int n_umax;        // list capacity per wave (>= any union size)
@@ -118,9 +119,11 @@ template <int D>
 __global__ __launch_bounds__(256) void tile_kv_kernel(const uint8_t* __restrict__ K,
                                                       const uint8_t* __restrict__ V,
                                                       uint8_t* __restrict__ Kt,
-                                                      uint8_t* __restrict__ Vt, int P) {
+                                                      uint8_t* __restrict__ Vt, int P, int Hkv,
+                                                      int h_begin, int h_count) {
   constexpr int KCH = D / 32, DT = D / 32;
-  const size_t blk = blockIdx.x;                   // page * H_kv + head
+  // one block per (page, head) of heads h_begin .. h_begin + h_count - 1
+  const size_t blk = (size_t)(blockIdx.x / h_count) * Hkv + h_begin + blockIdx.x % h_count;
   const uint8_t* kp = K + blk * P * D;
   const uint8_t* vp = V + blk * D * P;
   uint8_t* kt_out = Kt + blk * 64 * D;
@@ -175,8 +178,9 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   int my_t = -1, my_slot = -1;              // lane i < gm: member i's token (and slot)
 
   if constexpr (MODE == kUnionMode) {
-  h = gid / p.groups_per_head;
-  const int g0 = (gid - h * p.groups_per_head) * p.g;
+  const int hl = gid / p.groups_per_head;
+  h = p.h_begin + hl;
+  const int g0 = (gid - hl * p.groups_per_head) * p.g;
   gm = min(p.g, p.T - g0);
   const int nw = (p.N + 31) >> 5;              // words of the page bitset
   uint32_t* bits = reinterpret_cast<uint32_t*>(wbase + (size_t)p.n_umax * 4);
@@ -600,23 +604,26 @@ void common_params(UAParams& prm, const pw_shape& s, const uint16_t* Q, const fl
 size_t tiled_kv_bytes(const pw_shape& s) { return (size_t)2 * s.N_pages * s.H_kv * 64 * s.D; }
 
 hipError_t tile_kv(const pw_shape& s, const uint8_t* K, const uint8_t* V, uint8_t* tiles,
-                   hipStream_t stream) {
+                   hipStream_t stream, int h_begin, int h_count) {
+  if (h_count < 0) h_count = s.H_kv;
   uint8_t* Kt = tiles;
   uint8_t* Vt = tiles + tiled_kv_bytes(s) / 2;
-  const dim3 grid(s.N_pages * s.H_kv);
+  const dim3 grid(s.N_pages * h_count);
   if (s.D == 128)
-    hipLaunchKernelGGL(tile_kv_kernel<128>, grid, dim3(256), 0, stream, K, V, Kt, Vt, s.P);
+    hipLaunchKernelGGL(tile_kv_kernel<128>, grid, dim3(256), 0, stream, K, V, Kt, Vt, s.P, s.H_kv,
+                       h_begin, h_count);
   else
-    hipLaunchKernelGGL(tile_kv_kernel<64>, grid, dim3(256), 0, stream, K, V, Kt, Vt, s.P);
+    hipLaunchKernelGGL(tile_kv_kernel<64>, grid, dim3(256), 0, stream, K, V, Kt, Vt, s.P, s.H_kv,
+                       h_begin, h_count);
   return hipGetLastError();
 }
 
 hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
                                   const uint8_t* V, const float* scales, const int32_t* sel,
-                                  const int32_t* ids, int g, uint16_t* O, void* ws,
-                                  hipStream_t stream) {
+                                  const int32_t* ids, int g, int h_begin, int h_count,
+                                  uint16_t* O, void* ws, hipStream_t stream) {
   uint8_t* tiles = static_cast<uint8_t*>(ws);
-  hipError_t e = tile_kv(s, K, V, tiles, stream);
+  hipError_t e = tile_kv(s, K, V, tiles, stream, h_begin, h_count);
   if (e != hipSuccess) return e;
   UAParams prm;
   common_params(prm, s, Q, scales);
@@ -624,7 +631,8 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
   prm.Vt = tiles + tiled_kv_bytes(s) / 2;
   prm.sel = sel; prm.ids = ids; prm.O = O; prm.g = g;
   prm.groups_per_head = (s.T + g - 1) / g;
-  prm.total_groups = prm.groups_per_head * s.H_kv;
+  prm.total_groups = prm.groups_per_head * h_count;
+  prm.h_begin = h_begin;
   prm.n_umax = (g * s.S < s.N_pages) ? g * s.S : s.N_pages;
   const int nw = (s.N_pages + 31) / 32;           // page bitset words, then their list offsets
   prm.lds_wave = ((prm.n_umax * 4 + 2 * nw * 4) + 15) / 16 * 16;

@@ -48,6 +48,8 @@ _SIGS = {
     "pw_group": (_i32, [_SHP, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
     "pw_union_attention_workspace_bytes": (_sz, [_SHP, _i32]),
     "pw_union_attention": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "pw_union_attention_heads": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp,
+                                        _vp, _sz, _vp]),
     "pw_check_ids_workspace_bytes": (_sz, [_SHP]),
     "pw_check_ids": (_i32, [_SHP, _vp, _vp, _vp, _sz, _vp]),
     "pw_select_workspace_bytes": (_sz, [_SHP]),
@@ -125,7 +127,9 @@ def pw_union_attention_workspace_bytes(shp: PWShape, g: int = 8) -> int:
 
 def pw_union_attention(shp: PWShape, Q, K_fp8, V_fp8, scales, sel_pages, query_ids, g: int,
                        O: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
-                       stream=None) -> torch.Tensor:
+                       stream=None, heads: Optional[tuple] = None) -> torch.Tensor:
+    """Query-union attention; `heads` = (h_begin, h_count) restricts the call to those KV heads
+    (pw_union_attention_heads; the other rows of O are left untouched)."""
     T, Hq, Hkv, D, P, N, S = shp.T, shp.H_q, shp.H_kv, shp.D, shp.P, shp.N_pages, shp.S
     q = _dev(Q, "Q", _BF16, (T, Hq, D))
     k = _dev(K_fp8, "K_fp8", _U8, (N, Hkv, P, D))
@@ -140,9 +144,47 @@ def pw_union_attention(shp: PWShape, Q, K_fp8, V_fp8, scales, sel_pages, query_i
         workspace = torch.empty(pw_union_attention_workspace_bytes(shp, g), dtype=torch.uint8,
                                 device=Q.device)
     ws = _dev(workspace, "workspace", (torch.uint8,))
-    _check(_lib.pw_union_attention(ctypes.byref(shp), q, k, v, sc, sel, ids, g, o, ws,
-                                   workspace.numel(), _stream(stream)), "pw_union_attention")
+    if heads is None:
+        _check(_lib.pw_union_attention(ctypes.byref(shp), q, k, v, sc, sel, ids, g, o, ws,
+                                       workspace.numel(), _stream(stream)), "pw_union_attention")
+    else:
+        _check(_lib.pw_union_attention_heads(ctypes.byref(shp), q, k, v, sc, sel, ids, g,
+                                             int(heads[0]), int(heads[1]), o, ws,
+                                             workspace.numel(), _stream(stream)),
+               "pw_union_attention_heads")
     return O
+
+
+class HeadPipeline:
+    """The complete call (search, then attention) with the search of later KV heads
+    overlapping the attention of earlier ones: pw_group runs per chunk of `chunk` KV heads on
+    an auxiliary stream, and pw_union_attention_heads of each chunk waits for its search on
+    the caller's stream.  Only call ordering lives here (streams and events); every step is a
+    library call.  Streams keep the default priority."""
+
+    def __init__(self, shp: PWShape, chunk: int):
+        if shp.H_kv % chunk:
+            raise ValueError(f"chunk {chunk} does not divide H_kv = {shp.H_kv}")
+        self.shp, self.chunk = shp, chunk
+        G = shp.H_q // shp.H_kv
+        self.sub = PWShape(shp.T, G * chunk, chunk, shp.D, shp.P, shp.N_pages, shp.S)
+        self.aux = torch.cuda.Stream()
+        self.done = [torch.cuda.Event() for _ in range(shp.H_kv // chunk)]
+
+    def __call__(self, Q, K_fp8, V_fp8, scales, sel_pages, W: int, g: int,
+                 query_ids: torch.Tensor, O: torch.Tensor, workspace: torch.Tensor):
+        main = torch.cuda.current_stream()
+        self.aux.wait_stream(main)              # inputs are written on the caller's stream
+        c = self.chunk
+        for k, h0 in enumerate(range(0, self.shp.H_kv, c)):
+            pw_group(self.sub, sel_pages[h0:h0 + c], W, g, query_ids=query_ids[h0:h0 + c],
+                     stream=self.aux)
+            self.done[k].record(self.aux)
+        for k, h0 in enumerate(range(0, self.shp.H_kv, c)):
+            main.wait_event(self.done[k])
+            pw_union_attention(self.shp, Q, K_fp8, V_fp8, scales, sel_pages, query_ids, g, O=O,
+                               workspace=workspace, stream=main, heads=(h0, c))
+        return O
 
 
 def pw_check_ids(shp: PWShape, query_ids: torch.Tensor, stream=None) -> torch.Tensor:

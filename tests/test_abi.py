@@ -83,6 +83,17 @@ def test_attention_validation():
     assert f(ctypes.byref(shp), *[FAKE] * 6, 8, FAKE, ctypes.c_void_p(0x1010), need, None) == pw.PW_ERR_DIMS
 
 
+def test_head_range_validation():
+    f = pw._lib.pw_union_attention_heads
+    shp = _shape(H_kv=2, H_q=8)
+    need = pw._lib.pw_union_attention_workspace_bytes(ctypes.byref(shp), 8)
+    ws = ctypes.c_void_p(0x100000)
+    for h0, hc in [(-1, 1), (0, 0), (1, 2), (2, 1)]:
+        assert f(ctypes.byref(shp), *[FAKE] * 6, 8, h0, hc, FAKE, ws, need, None) == pw.PW_ERR_DIMS
+    assert f(ctypes.byref(shp), *[FAKE] * 6, 8, 0, 1, FAKE, ws, need - 1, None) == pw.PW_ERR_WORKSPACE
+    assert f(ctypes.byref(shp), *[FAKE] * 5, None, 8, 0, 1, FAKE, ws, need, None) == pw.PW_ERR_NULL
+
+
 def test_dense_union_validation():
     shp = _shape()
     f = pw._lib.pw_dense_union_ref

@@ -208,3 +208,51 @@ def test_side_streams_and_concurrent_calls():
     for i_s, o_s in zip(idss, outs):
         assert torch.equal(i_s, ids)
         assert torch.equal(o_s.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 4])
+def test_head_pipeline_matches_the_plain_call(chunk):
+    # search of later KV heads on a second stream while earlier heads attend: same IDs and
+    # the same output bits as pw_group + pw_union_attention on one stream
+    pw = _pw()
+    wl = synth.WORKLOADS["prefill_8k"]
+    log(f"[case] head pipeline prefill_8k chunk={chunk}")
+    dev = pw.to_device(host_inputs("prefill_8k"))
+    shp = pw.shape(*wl.shape_tuple())
+    ws = torch.empty(pw.pw_union_attention_workspace_bytes(shp, wl.g), dtype=torch.uint8,
+                     device="cuda")
+    ids_ref = pw.pw_group(shp, dev["sel_pages"], wl.W, wl.g)
+    O_ref = pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"],
+                                  dev["scales"], dev["sel_pages"], ids_ref, wl.g, workspace=ws)
+    run = pw.HeadPipeline(shp, chunk)
+    ids = torch.full_like(ids_ref, -7)
+    O = torch.zeros_like(O_ref)
+    for _ in range(2):                          # twice: events and streams are reused
+        run(dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"], dev["sel_pages"],
+            wl.W, wl.g, ids, O, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids_ref)
+    assert torch.equal(O.view(torch.int16), O_ref.view(torch.int16))
+
+
+def test_head_range_writes_only_its_heads():
+    pw = _pw()
+    log("[case] pw_union_attention_heads (1, 2) of 4 KV heads")
+    T, Hq, Hkv, D, P, S = 256, 8, 4, 64, 16, 6
+    inp = tiny_problem(T=T, Hq=Hq, Hkv=Hkv, D=D, P=P, S=S, seed=5)
+    dev = pw.to_device(inp)
+    shp = pw.shape(T, Hq, Hkv, D, P, T // P, S)
+    ids = torch.arange(T, dtype=torch.int32, device="cuda").repeat(Hkv, 1).contiguous()
+    O = torch.full((T, Hq, D), 3.0, dtype=torch.bfloat16, device="cuda")
+    pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
+                          dev["sel_pages"], ids, 8, O=O, heads=(1, 2))
+    torch.cuda.synchronize()
+    pairs = [(h, t) for h in (1, 2) for t in range(T)]
+    assert_close(gpu_rows(O, pairs, Hq // Hkv), oracle_rows(inp, pairs), "head range")
+    G = Hq // Hkv
+    untouched = torch.cat([O[:, :G], O[:, 3 * G:]], dim=1).float()
+    assert bool((untouched == 3.0).all())
+    with pytest.raises(pw.PWError) as e:
+        pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
+                              dev["sel_pages"], ids, 8, O=O, heads=(2, 3))
+    assert e.value.status == pw.PW_ERR_DIMS
