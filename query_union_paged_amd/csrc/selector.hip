@@ -17,7 +17,8 @@
 //   1. prep: qs (fp32 sum of the bf16 rows) and C (exact fp32 sum of the
 //      e4m3 codes) as bf16 hi + lo pairs;
 //   2. scores: <qs, C> for every (query, page <= own page) on the bf16 MFMA,
-//      hi*hi + hi*lo + lo*hi (relative error ~2^-16 of sum |qs||C|);
+//      hi*hi + hi*lo + lo*hi (relative error ~2^-16 of sum |qs||C|), 128 x 128
+//      tiles per workgroup with D staged through LDS;
 //   3. top-k: one wave per query, a 4-pass 8-bit radix select on the ordered
 //      fp32 score bits over LDS histograms, then the ascending row.
 #include "pw_internal.h"
@@ -50,71 +51,158 @@ __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
   lo = (__bf16)(x - (float)hi);
 }
 
-// qs and C of KV head h as bf16 hi/lo pairs: threads [0, T*D) do qs, the rest C.
+// qs and C of KV head h as bf16 hi/lo pairs, 8 d per thread (16-byte loads and
+// stores): threads [0, T*D/8) do qs, the rest C.
 __global__ __launch_bounds__(256) void sel_prep_kernel(const uint16_t* __restrict__ Q,
                                                        const uint8_t* __restrict__ K, int T,
                                                        int Hq, int Hkv, int D, int P, int N,
                                                        int h, __bf16* qh, __bf16* ql,
                                                        __bf16* ch, __bf16* cl) {
-  const int G = Hq / Hkv;
+  const int G = Hq / Hkv, D8 = D / 8;
   const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t nq = (size_t)T * D;
+  const size_t nq = (size_t)T * D8;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  __bf16 *hi, *lo;
   if (i < nq) {
-    const int t = (int)(i / D), d = (int)(i % D);
-    const uint16_t* q = Q + ((size_t)t * Hq + h * G) * D + d;
-    float acc = 0.f;
-    for (int j = 0; j < G; ++j) acc += __uint_as_float((uint32_t)q[(size_t)j * D] << 16);
-    split_bf16(acc, qh[i], ql[i]);
-  } else if (i < nq + (size_t)N * D) {
-    const size_t c = i - nq;
-    const int u = (int)(c / D), d = (int)(c % D);
-    const uint8_t* k = K + ((size_t)u * Hkv + h) * P * D + d;
-    float acc = 0.f;                  // every partial sum of e4m3 values here is exact in fp32
-    for (int j = 0; j < P; j += 2) {
-      const int pair = (int)k[(size_t)j * D] | ((int)k[(size_t)(j + 1) * D] << 8);
-      const auto f = __builtin_amdgcn_cvt_pk_f32_fp8(pair, false);
-      acc += f[0];
-      acc += f[1];
+    const int t = (int)(i / D8), d8 = (int)(i % D8);
+    const uint16_t* q = Q + ((size_t)t * Hq + h * G) * D + 8 * d8;
+    for (int j = 0; j < G; ++j) {
+      const uint4 v = *reinterpret_cast<const uint4*>(q + (size_t)j * D);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        acc[2 * k] += __uint_as_float(w[k] << 16);
+        acc[2 * k + 1] += __uint_as_float(w[k] & 0xFFFF0000u);
+      }
     }
-    split_bf16(acc, ch[c], cl[c]);
+    hi = qh + (size_t)t * D + 8 * d8;
+    lo = ql + (size_t)t * D + 8 * d8;
+  } else if (i < nq + (size_t)N * D8) {
+    const size_t c = i - nq;
+    const int u = (int)(c / D8), d8 = (int)(c % D8);
+    const uint8_t* k = K + ((size_t)u * Hkv + h) * P * D + 8 * d8;
+    for (int j = 0; j < P; ++j) {        // every partial sum of e4m3 values here is exact in fp32
+      const uint2 w = *reinterpret_cast<const uint2*>(k + (size_t)j * D);
+      const uint32_t ww[2] = {w.x, w.y};
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        const auto f01 = __builtin_amdgcn_cvt_pk_f32_fp8(ww[k2], false);
+        const auto f23 = __builtin_amdgcn_cvt_pk_f32_fp8(ww[k2], true);
+        acc[4 * k2] += f01[0];
+        acc[4 * k2 + 1] += f01[1];
+        acc[4 * k2 + 2] += f23[0];
+        acc[4 * k2 + 3] += f23[1];
+      }
+    }
+    hi = ch + (size_t)u * D + 8 * d8;
+    lo = cl + (size_t)u * D + 8 * d8;
+  } else {
+    return;
   }
+  bf16x8 vh, vl;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    __bf16 a, b;
+    split_bf16(acc[e], a, b);
+    vh[e] = a;
+    vl[e] = b;
+  }
+  *reinterpret_cast<bf16x8*>(hi) = vh;
+  *reinterpret_cast<bf16x8*>(lo) = vl;
 }
 
-// scores[t][u] = <qs_t, C_u> for one 32 x 32 (query, page) tile per wave; tiles
-// whose pages all lie after the tile's last query are skipped.
+// scores[t][u] = <qs_t, C_u> for one 128 x 128 (query, page) tile per workgroup;
+// tiles whose pages all lie after the tile's last query exit.  D is staged in
+// LDS 32 at a time (the next slice's loads in flight during the current one's
+// MFMAs); each wave owns a 64 x 64 quarter as 2 x 2 MFMA tiles, three MFMAs
+// per 16-d step (lo*hi + hi*lo + hi*hi).
+constexpr int kSelTile = 128;
+constexpr int kSelKD = 32;                    // d per staged slice
+constexpr int kSelStride = kSelKD + 8;        // LDS row stride in bf16 (conflict-spreading pad)
+
 __global__ __launch_bounds__(256) void sel_score_kernel(const __bf16* __restrict__ qh,
                                                         const __bf16* __restrict__ ql,
                                                         const __bf16* __restrict__ ch,
                                                         const __bf16* __restrict__ cl, int T,
                                                         int D, int P, int N, int n_ut,
                                                         float* __restrict__ sc) {
-  const int lane = threadIdx.x & 63;
-  const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int tt = wid / n_ut, ut = wid % n_ut;
-  const int t0 = 32 * tt, u0 = 32 * ut;
-  if (t0 >= T || u0 > (min(T, t0 + 32) - 1) / P) return;
+  __shared__ __align__(16) __bf16 lds[4][kSelTile * kSelStride];   // qh, ql, ch, cl slices
+  const int tt = blockIdx.x / n_ut, ut = blockIdx.x % n_ut;
+  const int t0 = kSelTile * tt, u0 = kSelTile * ut;
+  if (u0 > (min(T, t0 + kSelTile) - 1) / P) return;               // uniform: all after the tile
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wy = wave >> 1, wx = wave & 1;
   const int row = lane & 31, half = lane >> 5;
-  const int t = min(t0 + row, T - 1), u = min(u0 + row, N - 1);
-  f32x16 acc;
+  const __bf16* src[4] = {qh, ql, ch, cl};
+  // loader: 4 arrays x 128 rows x 4 segments of 8 bf16; thread covers segments tid, tid + 256
+  uint4 pre[4][2];
+  auto load = [&](int d0) __attribute__((always_inline)) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-  for (int k0 = 0; k0 < D; k0 += 16) {
-    const size_t qo = (size_t)t * D + k0 + 8 * half, co = (size_t)u * D + k0 + 8 * half;
-    const bf16x8 a_h = *reinterpret_cast<const bf16x8*>(qh + qo);
-    const bf16x8 a_l = *reinterpret_cast<const bf16x8*>(ql + qo);
-    const bf16x8 b_h = *reinterpret_cast<const bf16x8*>(ch + co);
-    const bf16x8 b_l = *reinterpret_cast<const bf16x8*>(cl + co);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_l, b_h, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_h, b_l, acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_h, b_h, acc, 0, 0, 0);
-  }
-  // lane holds column u0 + row, rows 8*(r/4) + 4*half + r%4 of the tile
-  const int uc = u0 + row;
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int tr = t0 + 8 * (r >> 2) + 4 * half + (r & 3);
-    if (tr < T && uc < N) sc[(size_t)tr * N + uc] = acc[r];
+      for (int j = 0; j < 2; ++j) {
+        const int sidx = tid + 256 * j, r = sidx >> 2, part = sidx & 3;
+        const int g = (a < 2 ? t0 : u0) + r;
+        const int lim = a < 2 ? T : N;
+        pre[a][j] = g < lim ? *reinterpret_cast<const uint4*>(src[a] + (size_t)g * D + d0 + 8 * part)
+                            : make_uint4(0, 0, 0, 0);
+      }
+  };
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  load(0);
+  for (int d0 = 0; d0 < D; d0 += kSelKD) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int sidx = tid + 256 * j, r = sidx >> 2, part = sidx & 3;
+        *reinterpret_cast<uint4*>(&lds[a][r * kSelStride + 8 * part]) = pre[a][j];
+      }
+    __syncthreads();
+    if (d0 + kSelKD < D) load(d0 + kSelKD);
+#pragma unroll
+    for (int k0 = 0; k0 < kSelKD; k0 += 16) {
+      bf16x8 ah[2], al[2], bh[2], bl[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int ra = 64 * wy + 32 * i + row, rb = 64 * wx + 32 * i + row;
+        const int o = k0 + 8 * half;
+        ah[i] = *reinterpret_cast<const bf16x8*>(&lds[0][ra * kSelStride + o]);
+        al[i] = *reinterpret_cast<const bf16x8*>(&lds[1][ra * kSelStride + o]);
+        bh[i] = *reinterpret_cast<const bf16x8*>(&lds[2][rb * kSelStride + o]);
+        bl[i] = *reinterpret_cast<const bf16x8*>(&lds[3][rb * kSelStride + o]);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], bh[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bl[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[i], bh[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    __syncthreads();                      // the slice is overwritten next
   }
+  // lane holds column (page) row of each 32 x 32 tile, rows 8*(r/4) + 4*half + r%4
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int uc = u0 + 64 * wx + 32 * j + row;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int tr = t0 + 64 * wy + 32 * i + 8 * (r >> 2) + 4 * half + (r & 3);
+        if (tr < T && uc < N) sc[(size_t)tr * N + uc] = acc[i][j][r];
+      }
+    }
 }
 
 // Larger float -> larger key (fp32 bits made unsigned-ordered).
@@ -233,12 +321,12 @@ hipError_t launch_select(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
   __bf16* ch = reinterpret_cast<__bf16*>(base + l.off_ch);
   __bf16* cl = reinterpret_cast<__bf16*>(base + l.off_cl);
   float* sc = reinterpret_cast<float*>(base + l.off_sc);
-  const int n_tt = (s.T + 31) / 32, n_ut = (s.N_pages + 31) / 32;
-  const size_t n_prep = (size_t)(s.T + s.N_pages) * s.D;
+  const int n_tt = (s.T + kSelTile - 1) / kSelTile, n_ut = (s.N_pages + kSelTile - 1) / kSelTile;
+  const size_t n_prep = (size_t)(s.T + s.N_pages) * (s.D / 8);
   for (int h = 0; h < s.H_kv; ++h) {
     hipLaunchKernelGGL(sel_prep_kernel, dim3((unsigned)((n_prep + 255) / 256)), dim3(256), 0,
                        stream, Q, K, s.T, s.H_q, s.H_kv, s.D, s.P, s.N_pages, h, qh, ql, ch, cl);
-    hipLaunchKernelGGL(sel_score_kernel, dim3((n_tt * n_ut + 3) / 4), dim3(256), 0, stream, qh,
+    hipLaunchKernelGGL(sel_score_kernel, dim3(n_tt * n_ut), dim3(256), 0, stream, qh,
                        ql, ch, cl, s.T, s.D, s.P, s.N_pages, n_ut, sc);
     hipLaunchKernelGGL(sel_topk_kernel, dim3((s.T + 3) / 4), dim3(256), 0, stream, sc,
                        scales + h, s.T, s.H_kv, s.P, s.N_pages, s.S, L, h, sel);
