@@ -83,6 +83,7 @@ __global__ __launch_bounds__(256) void sel_prep_kernel(const uint16_t* __restric
     const size_t c = i - nq;
     const int u = (int)(c / D8), d8 = (int)(c % D8);
     const uint8_t* k = K + ((size_t)u * Hkv + h) * P * D + 8 * d8;
+#pragma unroll 8
     for (int j = 0; j < P; ++j) {        // every partial sum of e4m3 values here is exact in fp32
       const uint2 w = *reinterpret_cast<const uint2*>(k + (size_t)j * D);
       const uint32_t ww[2] = {w.x, w.y};
