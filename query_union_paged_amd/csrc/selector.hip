@@ -230,14 +230,26 @@ __global__ __launch_bounds__(256) void sel_topk_kernel(const float* __restrict__
   constexpr int R = kMaxPages / 64;
   uint32_t key[R];
   uint32_t valid = 0, chosen = 0;                  // bit i: page lane + 64 i
+  // all loads first (clamped to the row, so none needs a branch), then the keys
+  float sv[R], kv[R];
+  const int n_load = min(lo_local, N);             // candidates lie below lo_local
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    const int u = min(lane + 64 * i, N - 1);
+    if (64 * i < n_load) {                         // uniform: skip chunks past the candidates
+      sv[i] = sc[(size_t)t * N + u];
+      kv[i] = kscale[(size_t)u * Hkv];
+    } else {
+      sv[i] = 0.f;
+      kv[i] = 0.f;
+    }
+  }
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     const int u = lane + 64 * i;
-    key[i] = 0;
-    if (u >= 1 && u < lo_local) {
-      key[i] = order_key(sc[(size_t)t * N + u] * kscale[(size_t)u * Hkv]);
-      valid |= 1u << i;
-    }
+    const bool ok = u >= 1 && u < lo_local;
+    key[i] = ok ? order_key(sv[i] * kv[i]) : 0u;
+    valid |= ok ? 1u << i : 0u;
   }
   if (k > 0) {
     uint32_t prefix = 0, mask = 0;
