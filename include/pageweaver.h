@@ -156,7 +156,10 @@ pw_status pw_check_ids(const pw_shape* shape, const int32_t* query_ids, int32_t*
  *      unwritten.
  * Out: O.
  * Support set: D in {64, 128}; P in {16, 32, 64}; N_pages <= 32768; the
- * re-tiled K (and V) copy below at most 2 GiB.
+ * re-tiled K (and V) copy below at most 2 GiB.  Value range: the online
+ * softmax works in fp32 base-2 logits, |<Q, Khat>| * log2(e) / sqrt(D) <
+ * 2^20 (about 7e5 in natural units); beyond that an fp32 reference maximum
+ * cannot resolve a row and the output is unspecified.
  * Workspace: pw_union_attention_workspace_bytes() = 2 * N_pages * H_kv * 64 * D
  * bytes, 256-byte aligned, required.  Each call first re-tiles the FP8 K and V
  * pages into it in matrix-core operand order (64 key slots per page, keys

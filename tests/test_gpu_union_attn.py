@@ -256,3 +256,32 @@ def test_head_range_writes_only_its_heads():
         pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
                               dev["sel_pages"], ids, 8, O=O, heads=(2, 3))
     assert e.value.status == pw.PW_ERR_DIMS
+
+
+def test_extreme_magnitudes():
+    # Q rows scaled by 2^-40 .. 2^4 (the per-row power-of-two split must keep them exact) and
+    # K scales from 1e-4 to 10 (very flat to very peaked softmax rows, logits up to ~1e4 in
+    # log2 units; the documented range is |logit| < 2^20), V scales unchanged
+    log("[case] union extreme Q magnitudes and K scales")
+    T, P, Hq, Hkv, D, S = 256, 16, 8, 2, 128, 7
+    inp = tiny_problem(T=T, Hq=Hq, Hkv=Hkv, D=D, P=P, S=S, seed=91)
+    q = torch.from_numpy(inp["q_bits"].view(np.int16)).view(torch.bfloat16).float()
+    e = torch.from_numpy(np.random.default_rng(1).integers(-40, 5, size=(T, Hq, 1))).float()
+    q = (q * torch.exp2(e)).to(torch.bfloat16)
+    sc = inp["scales"].copy()
+    sc[0] = np.exp(np.random.default_rng(2).uniform(np.log(1e-4), np.log(10.0), size=sc[0].shape))
+    inp = dict(inp, q_bits=q.view(torch.int16).numpy().view(np.uint16), scales=sc.astype(np.float32))
+    O, _ = _run(inp, 8, "regroup", 32)
+    pairs = _all_pairs(Hkv, T)
+    assert_close(gpu_rows(O, pairs, Hq // Hkv), oracle_rows(inp, pairs), "extreme magnitudes")
+
+
+@pytest.mark.parametrize("T,P,g,W", [(16, 16, 16, 16), (16, 16, 8, 16), (32, 16, 1, 32), (64, 64, 4, 64)])
+def test_minimal_shapes(T, P, g, W):
+    # one or two pages, a window equal to the sequence, groups of one or of the whole sequence
+    log(f"[case] union minimal T={T} P={P} g={g} W={W}")
+    inp = tiny_problem(T=T, Hq=4, Hkv=1, D=64, P=P, S=2, seed=T + g)
+    O, ids = _run(inp, g, "regroup", W)
+    assert sorted(ids.cpu().numpy()[0].tolist()) == list(range(T))
+    pairs = _all_pairs(1, T)
+    assert_close(gpu_rows(O, pairs, 4), oracle_rows(inp, pairs), f"minimal T={T} g={g}")
