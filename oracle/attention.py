@@ -28,7 +28,7 @@ from __future__ import annotations
 
 import math
 import os
-from typing import Iterable, Optional, Sequence
+from typing import Optional, Sequence
 
 import numpy as np
 

@@ -3,7 +3,6 @@
 CPU only: every call here returns its status before any HIP call is made.
 """
 import ctypes
-import os
 import subprocess
 
 import pytest

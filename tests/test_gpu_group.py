@@ -8,7 +8,6 @@ import torch
 from query_union_paged_amd import synth
 from oracle.greedy import group_ids
 from tests.gpu_common import WORKERS, host_inputs, log
-from tests.oracle_helpers import tiny_problem
 
 pytestmark = pytest.mark.gpu
 

@@ -12,7 +12,6 @@ import numpy as np
 import pytest
 import torch
 
-from oracle.fp8 import decode_bf16, decode_e4m3fn
 from oracle.selector import fixed_pages, query_sums, key_sums
 from query_union_paged_amd import synth
 from tests.gpu_common import assert_close, gpu_rows, log, oracle_rows

@@ -1,5 +1,4 @@
 """Pins of the fp64 attention oracle (CPU only)."""
-import math
 
 import numpy as np
 import pytest
