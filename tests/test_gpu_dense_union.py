@@ -114,3 +114,14 @@ def test_page_pairs_random(T, P, S, seed):
     got = got.cpu().numpy()
     assert np.array_equal(got, again.cpu().numpy())
     _assert_pairs(got, _oracle_pairs(sel, N, range(2)), N)
+
+
+@pytest.mark.parametrize("D,P,Hq,Hkv,S", [(64, 16, 4, 1, 8), (128, 32, 8, 2, 5)])
+def test_dense_affinity_shapes(D, P, Hq, Hkv, S):
+    log(f"[case] dense affinity shape D={D} P={P} Hq={Hq} Hkv={Hkv} S={S}")
+    T = 32 * P
+    inp = tiny_problem(T=T, Hq=Hq, Hkv=Hkv, D=D, P=P, S=S, seed=D + P + S)
+    O, got = _run_dense(inp, affinity=True)
+    _assert_pairs(got, _oracle_pairs(inp["sel_pages"], T // P, range(Hkv)), T // P)
+    pairs = [(h, t) for h in range(Hkv) for t in range(T)]
+    assert_close(gpu_rows(O, pairs, Hq // Hkv), oracle_rows(inp, pairs), f"dense affinity D{D} P{P}")

@@ -285,3 +285,14 @@ def test_minimal_shapes(T, P, g, W):
     assert sorted(ids.cpu().numpy()[0].tolist()) == list(range(T))
     pairs = _all_pairs(1, T)
     assert_close(gpu_rows(O, pairs, 4), oracle_rows(inp, pairs), f"minimal T={T} g={g}")
+
+
+@pytest.mark.parametrize("W,g", [(512, 8), (1024, 16)])
+def test_wide_window_pipeline(W, g):
+    # a wide search window (several waves per window) feeding the attention
+    wl = synth.WORKLOADS["prefill_8k"]
+    log(f"[case] union prefill_8k regrouped with W={W} g={g}")
+    inp = host_inputs("prefill_8k")
+    O, ids = _run(inp, g, "regroup", W)
+    rows = sample_pairs(wl)
+    assert_close(gpu_rows(O, rows, wl.G), oracle_rows(inp, rows), f"wide window W={W} g={g}")
