@@ -296,3 +296,29 @@ def test_wide_window_pipeline(W, g):
     O, ids = _run(inp, g, "regroup", W)
     rows = sample_pairs(wl)
     assert_close(gpu_rows(O, rows, wl.G), oracle_rows(inp, rows), f"wide window W={W} g={g}")
+
+
+def test_disjoint_head_ranges_share_a_workspace_concurrently():
+    # two streams, KV heads [0, 4) and [4, 8), one workspace: the same bits as one full call
+    pw = _pw()
+    wl = synth.WORKLOADS["prefill_8k"]
+    log("[case] pw_union_attention_heads on two streams with one workspace")
+    dev = pw.to_device(host_inputs("prefill_8k"))
+    shp = pw.shape(*wl.shape_tuple())
+    ws = torch.empty(pw.pw_union_attention_workspace_bytes(shp, wl.g), dtype=torch.uint8,
+                     device="cuda")
+    ids = pw.pw_group(shp, dev["sel_pages"], wl.W, wl.g)
+    args = (shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"], dev["sel_pages"],
+            ids, wl.g)
+    O_ref = pw.pw_union_attention(*args, workspace=ws)
+    torch.cuda.synchronize()
+    ws.zero_()
+    O = torch.zeros_like(O_ref)
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    for _ in range(3):
+        pw.pw_union_attention(*args, O=O, workspace=ws, stream=s1, heads=(0, 4))
+        pw.pw_union_attention(*args, O=O, workspace=ws, stream=s2, heads=(4, 4))
+    torch.cuda.synchronize()
+    assert torch.equal(O.view(torch.int16), O_ref.view(torch.int16))
