@@ -526,15 +526,13 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
     const float ks_c = ksr, vs_c = vsr;
     const int u1 = page_of(up + 1);
     qk(kbuf, sacc);
-    __builtin_amdgcn_sched_barrier(0);    // K registers are free after the MFMAs read them
-    load_k(kbuf, u1);
+    load_k(kbuf, u1);                     // K registers are free once the MFMAs have read them
     ksr = kscale[(size_t)u1 * p.Hkv];
     vsr = vscale[(size_t)u1 * p.Hkv];
     mask_page(sacc, ent & 0xFFFF);
     softmax(sacc, ent >> 16, ks_c, vs_c, pB, alph);
     rescale(alph);
     pv(vbuf, pB);
-    __builtin_amdgcn_sched_barrier(0);
     load_v(vbuf, u1);
   }
 
