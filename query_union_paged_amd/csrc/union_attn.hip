@@ -18,7 +18,9 @@
 //                          the columns, so each lane holds one query row
 //                          (lane & 31) and 32 of its 64 keys;
 //   online softmax         fp32 in registers, log2 domain, lazy rescale; row
-//                          max/sum finished with one cross-half lane swap;
+//                          max/sum finished with one cross-half lane swap; the
+//                          max pass is skipped when |q| * max |k| shows that no
+//                          score of the page can move any row's reference;
 //   O^T += V_page^T * P^T  v_mfma_f32_32x32x16_bf16 with the V codes converted
 //                          to bf16 exactly; d is the MFMA row.
 // Page loads are contiguous 1 KB wave reads of the tiled copy straight into
@@ -42,13 +44,22 @@ namespace pw {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kTau = 8.0f;   // lazy-rescale threshold (log2 units): p <= 2^8
+// Lazy-rescale threshold (log2 units): a row's reference maximum moves only
+// when a score exceeds it by more than kTau, so p <= 2^kTau.  At 24, the
+// Cauchy-Schwarz bound below usually proves on N(0,1)-like data that no score
+// of a page can move the reference, and the wave skips its max pass.
+constexpr float kTau = 24.0f;
+// Relative slack of the norm bounds: covers the fp32 rounding of the sums of
+// squares, of the square roots and of the score accumulation, and the residual
+// of the two-part e4m3 split of Q (below 1e-4 of a row's norm).
+constexpr float kNormSlack = 1.0f + 1.0f / 512;
 
 struct UAParams {
   const uint16_t* Q;
   const uint8_t* Kt;   // tiled copies of the FP8 K and V pages (see tile_kv_kernel)
   const uint8_t* Vt;
   const float* scales;
+  const float* kn;     // [N][Hkv]: largest key norm of each K page, in code units
   const int32_t* sel;
   const int32_t* ids;
   uint16_t* O;
@@ -115,11 +126,15 @@ __device__ __forceinline__ uint4 load16(const uint8_t* p) {
 // at byte 16 * ((kt * D/32 + c) * 64 + l), resp. 16 * ((2 dt + j) * 64 + l);
 // key slots >= P are zero.  The attention loop then reads each page with
 // contiguous 1 KB wave loads instead of one 128-byte row per lane.
+// The same pass stores kn[u][h] = (1 + 2^-9) * max over the page's keys of the
+// Euclidean norm of the decoded e4m3 codes (no scale): with the norm of a query
+// row it bounds every score of that row on the page.
 template <int D>
 __global__ __launch_bounds__(256) void tile_kv_kernel(const uint8_t* __restrict__ K,
                                                       const uint8_t* __restrict__ V,
                                                       uint8_t* __restrict__ Kt,
-                                                      uint8_t* __restrict__ Vt, int P, int Hkv,
+                                                      uint8_t* __restrict__ Vt,
+                                                      float* __restrict__ kn, int P, int Hkv,
                                                       int h_begin, int h_count) {
   constexpr int KCH = D / 32, DT = D / 32;
   // one block per (page, head) of heads h_begin .. h_begin + h_count - 1
@@ -142,6 +157,34 @@ __global__ __launch_bounds__(256) void tile_kv_kernel(const uint8_t* __restrict_
                              : make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4*>(vt_out + 16 * q) = v;
   }
+  // key norms: four threads per key slot, D / 4 codes each
+  __shared__ float wmax[4];
+  const int key = threadIdx.x >> 2, part = threadIdx.x & 3;
+  float ss = 0.f;
+  if (key < P) {
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) {
+      const uint4 v = load16(kp + (size_t)key * D + (D / 4) * part + 16 * c);
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], false);
+        const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w[k], true);
+        ss = fmaf(a[0], a[0], ss);
+        ss = fmaf(a[1], a[1], ss);
+        ss = fmaf(b[0], b[0], ss);
+        ss = fmaf(b[1], b[1], ss);
+      }
+    }
+  }
+  ss += __shfl_xor(ss, 1);
+  ss += __shfl_xor(ss, 2);
+#pragma unroll
+  for (int o = 4; o < 64; o <<= 1) ss = fmaxf(ss, __shfl_xor(ss, o));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  if (threadIdx.x == 0)
+    kn[blk] = sqrtf(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))) * kNormSlack;
 }
 
 // MODE kUnionMode: groups of query IDs, union of their selected pages, O out.
@@ -290,7 +333,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   // from the cache bytes; 2^-e is folded back into the score scale.
   constexpr int KQ = D / 64;     // fp8 MFMA k-steps (64 d each, 32 per lane half)
   int slot[NT], trow[NT], qhead[NT], pslot[NT];
-  float rscale[NT];
+  float rscale[NT], qn[NT];      // qn: bound on the norm of the row's hi + lo (scaled)
   i32x8 qhi[NT][KQ], qlo[NT][KQ];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -325,6 +368,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
       e = 8 - ex;                  // amax * 2^e in [128, 256)
     }
     rscale[nt] = ldexpf(1.f, -e);
+    float ssq = 0.f;
 #pragma unroll
     for (int ks = 0; ks < KQ; ++ks) {
 #pragma unroll
@@ -332,6 +376,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
         const float* x = q + 32 * ks + 4 * w;
         const float x0 = ldexpf(x[0], e), x1 = ldexpf(x[1], e);
         const float x2 = ldexpf(x[2], e), x3 = ldexpf(x[3], e);
+        ssq = fmaf(x0, x0, fmaf(x1, x1, fmaf(x2, x2, fmaf(x3, x3, ssq))));
         int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
         hi = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hi, true);
         const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
@@ -342,6 +387,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
         qlo[nt][ks][w] = lo;
       }
     }
+    qn[nt] = sqrtf(ssq + __shfl_xor(ssq, 32)) * kNormSlack;
   }
 
   float m_run[NT], l_run[NT];
@@ -361,7 +407,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   // below is one contiguous 1 KB read of the wave (lane l at 16 * l).
   uint4 kbuf[2][KCH], vbuf[DT][2];
   f32x16 sacc[NT][2];
-  float ksr = 0.f, vsr = 0.f;
+  float ksr = 0.f, vsr = 0.f, knr = 0.f;
   auto page_of = [&](int i) {       // wave-uniform
     return __builtin_amdgcn_readfirstlane((int)(list[min(i, n_u - 1)] & 0xFFFF));
   };
@@ -394,6 +440,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   };
   const float* kscale = p.scales + h;                       // [N][Hkv]
   const float* vscale = p.scales + (size_t)p.N * p.Hkv + h;
+  const float* knorm = p.kn + h;                            // [N][Hkv]
   // S^T = K (Qhi + Qlo)^T on the FP8 MFMA
   auto qk = [&](const uint4 (&kr)[2][KCH], f32x16 (&sc)[NT][2]) {
 #pragma unroll
@@ -442,23 +489,33 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   // probabilities are produced as bf16 MFMA operands; returns the rescale
   // factor of the accumulator (1 unless the reference max moved)
   auto softmax = [&](f32x16 (&sc)[NT][2], uint32_t mbits, float ks_raw, float vs_raw,
-                     bf16x8 (&pB)[NT][4], float (&alph)[NT]) {
+                     float kn_raw, bf16x8 (&pB)[NT][4], float (&alph)[NT]) {
     const float ksc0 = ks_raw * p.qk_scale;
+    const float kb0 = kn_raw * fabsf(ksc0);
     const float lvs = __builtin_amdgcn_logf(vs_raw);    // log2
     const float ivs = __builtin_amdgcn_rcpf(vs_raw);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      float mx = max_raw(sc[nt][0][0], sc[nt][0][1]);
-#pragma unroll
-      for (int i = 2; i < 32; i += 2)
-        mx = max3_raw(mx, sc[nt][i >> 4][i & 15], sc[nt][i >> 4][(i & 15) + 1]);
-      mx = half_max(mx);
       const bool member = slot[nt] >= 0 && ((mbits >> slot[nt]) & 1u);
       const float ksc = ksc0 * rscale[nt];
-      const float mx2 = mx * ksc;
-      const float m_new = (member && mx2 > m_run[nt] + kTau) ? mx2 : m_run[nt];
-      // branch-free: exp2(0) = 1 exactly when the reference max is unchanged
-      const float alpha = __builtin_amdgcn_exp2f((m_new == m_run[nt]) ? 0.f : m_run[nt] - m_new);
+      const float lim = m_run[nt] + kTau;
+      // Cauchy-Schwarz: no score of the row on this page exceeds
+      // |q| * max |k| * |scale|; when that cannot pass the reference by kTau
+      // for any member row, the row maxima are not needed (the computed
+      // maximum would leave every reference where it is: same result).
+      const bool may_move = member && !(qn[nt] * kb0 * rscale[nt] <= lim);
+      float m_new = m_run[nt], alpha = 1.f;
+      if (__ballot(may_move)) {
+        float mx = max_raw(sc[nt][0][0], sc[nt][0][1]);
+#pragma unroll
+        for (int i = 2; i < 32; i += 2)
+          mx = max3_raw(mx, sc[nt][i >> 4][i & 15], sc[nt][i >> 4][(i & 15) + 1]);
+        mx = half_max(mx);
+        const float mx2 = mx * ksc;
+        m_new = (member && mx2 > lim) ? mx2 : m_run[nt];
+        // exp2(0) = 1 exactly when the reference max is unchanged
+        alpha = __builtin_amdgcn_exp2f((m_new == m_run[nt]) ? 0.f : m_run[nt] - m_new);
+      }
       m_run[nt] = m_new;
       const float bias = (member && m_new > -INFINITY) ? (lvs - m_new) : -INFINITY;
       float ps = 0.f;
@@ -518,19 +575,21 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
     load_v(vbuf, u0);
     ksr = kscale[(size_t)u0 * p.Hkv];
     vsr = vscale[(size_t)u0 * p.Hkv];
+    knr = knorm[(size_t)u0 * p.Hkv];
   }
   bf16x8 pB[NT][4];
   float alph[NT];
   for (int up = 0; up < n_u; ++up) {
     const uint32_t ent = __builtin_amdgcn_readfirstlane(list[up]);
-    const float ks_c = ksr, vs_c = vsr;
+    const float ks_c = ksr, vs_c = vsr, kn_c = knr;
     const int u1 = page_of(up + 1);
     qk(kbuf, sacc);
     load_k(kbuf, u1);                     // K registers are free once the MFMAs have read them
     ksr = kscale[(size_t)u1 * p.Hkv];
     vsr = vscale[(size_t)u1 * p.Hkv];
+    knr = knorm[(size_t)u1 * p.Hkv];
     mask_page(sacc, ent & 0xFFFF);
-    softmax(sacc, ent >> 16, ks_c, vs_c, pB, alph);
+    softmax(sacc, ent >> 16, ks_c, vs_c, kn_c, pB, alph);
     rescale(alph);
     pv(vbuf, pB);
     load_v(vbuf, u1);
@@ -599,20 +658,25 @@ void common_params(UAParams& prm, const pw_shape& s, const uint16_t* Q, const fl
 
 }  // namespace
 
-size_t tiled_kv_bytes(const pw_shape& s) { return (size_t)2 * s.N_pages * s.H_kv * 64 * s.D; }
+// Workspace of the re-tiled pages: K tiles, V tiles, then the page key norms.
+size_t tiled_kn_offset(const pw_shape& s) { return (size_t)2 * s.N_pages * s.H_kv * 64 * s.D; }
+size_t tiled_kv_bytes(const pw_shape& s) {
+  return tiled_kn_offset(s) + ((size_t)4 * s.N_pages * s.H_kv + 255) / 256 * 256;
+}
 
 hipError_t tile_kv(const pw_shape& s, const uint8_t* K, const uint8_t* V, uint8_t* tiles,
                    hipStream_t stream, int h_begin, int h_count) {
   if (h_count < 0) h_count = s.H_kv;
   uint8_t* Kt = tiles;
-  uint8_t* Vt = tiles + tiled_kv_bytes(s) / 2;
+  uint8_t* Vt = tiles + tiled_kn_offset(s) / 2;
+  float* kn = reinterpret_cast<float*>(tiles + tiled_kn_offset(s));
   const dim3 grid(s.N_pages * h_count);
   if (s.D == 128)
-    hipLaunchKernelGGL(tile_kv_kernel<128>, grid, dim3(256), 0, stream, K, V, Kt, Vt, s.P, s.H_kv,
-                       h_begin, h_count);
+    hipLaunchKernelGGL(tile_kv_kernel<128>, grid, dim3(256), 0, stream, K, V, Kt, Vt, kn, s.P,
+                       s.H_kv, h_begin, h_count);
   else
-    hipLaunchKernelGGL(tile_kv_kernel<64>, grid, dim3(256), 0, stream, K, V, Kt, Vt, s.P, s.H_kv,
-                       h_begin, h_count);
+    hipLaunchKernelGGL(tile_kv_kernel<64>, grid, dim3(256), 0, stream, K, V, Kt, Vt, kn, s.P,
+                       s.H_kv, h_begin, h_count);
   return hipGetLastError();
 }
 
@@ -626,7 +690,8 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
   UAParams prm;
   common_params(prm, s, Q, scales);
   prm.Kt = tiles;
-  prm.Vt = tiles + tiled_kv_bytes(s) / 2;
+  prm.Vt = tiles + tiled_kn_offset(s) / 2;
+  prm.kn = reinterpret_cast<const float*>(tiles + tiled_kn_offset(s));
   prm.sel = sel; prm.ids = ids; prm.O = O; prm.g = g;
   prm.groups_per_head = (s.T + g - 1) / g;
   prm.total_groups = prm.groups_per_head * h_count;
@@ -649,7 +714,8 @@ hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uin
   UAParams prm;
   common_params(prm, s, Q, scales);
   prm.Kt = tiles;
-  prm.Vt = tiles + tiled_kv_bytes(s) / 2;
+  prm.Vt = tiles + tiled_kn_offset(s) / 2;
+  prm.kn = reinterpret_cast<const float*>(tiles + tiled_kn_offset(s));
   prm.plist = plist; prm.pcount = pcount; prm.partials = partials;
   prm.tstart = tstart; prm.pairs = pairs; prm.tiles_head = tiles_head;
   prm.Np = Np; prm.Tc = Tc; prm.t0 = t0;

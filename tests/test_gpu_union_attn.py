@@ -276,6 +276,27 @@ def test_extreme_magnitudes():
     assert_close(gpu_rows(O, pairs, Hq // Hkv), oracle_rows(inp, pairs), "extreme magnitudes")
 
 
+def test_moving_reference_maximum():
+    # K scales that jump by 2^0 .. 2^12 from page to page: the row maxima of some pages pass the
+    # running reference by more than the lazy threshold (rescales), those of the pages after a
+    # jump cannot (the norm bound lets the wave skip its max pass); all within tolerance, and
+    # regrouped, identity and g = 1 rows stay bit-identical
+    log("[case] union moving reference maximum")
+    T, P, Hq, Hkv, D, S = 512, 16, 8, 2, 128, 12
+    inp = tiny_problem(T=T, Hq=Hq, Hkv=Hkv, D=D, P=P, S=S, seed=93)
+    sc = inp["scales"].copy()
+    N = sc.shape[1]
+    sc[0] = sc[0] * np.exp2(2.0 * (np.arange(N) % 7))[:, None]
+    inp = dict(inp, scales=sc.astype(np.float32))
+    O, _ = _run(inp, 8, "regroup", 64)
+    pairs = _all_pairs(Hkv, T)
+    assert_close(gpu_rows(O, pairs, Hq // Hkv), oracle_rows(inp, pairs), "moving reference")
+    O_id, _ = _run(inp, 8, "identity")
+    O_1, _ = _run(inp, 1, "identity")
+    assert torch.equal(O.view(torch.int16), O_id.view(torch.int16))
+    assert torch.equal(O.view(torch.int16), O_1.view(torch.int16))
+
+
 @pytest.mark.parametrize("T,P,g,W", [(16, 16, 16, 16), (16, 16, 8, 16), (32, 16, 1, 32), (64, 64, 4, 64)])
 def test_minimal_shapes(T, P, g, W):
     # one or two pages, a window equal to the sequence, groups of one or of the whole sequence
