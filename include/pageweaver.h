@@ -162,12 +162,13 @@ pw_status pw_check_ids(const pw_shape* shape, const int32_t* query_ids, int32_t*
  * fp32 reference maximum cannot resolve a row (or the unnormalised sums
  * overflow) and the output is unspecified.
  * Workspace: pw_union_attention_workspace_bytes() = 2 * N_pages * H_kv * 64 * D
- * + 4 * N_pages * H_kv (rounded up to 256) bytes, 256-byte aligned, required.
+ * + 16 * N_pages * H_kv (rounded up to 256) bytes, 256-byte aligned, required.
  * Each call first re-tiles the FP8 K and V pages into it in matrix-core operand
  * order (64 key slots per page, keys >= P zero), so that every page load of the
- * attention loop is a contiguous 1 KB wave read, and stores each K page's
- * largest key norm (which lets the softmax skip row maxima that cannot move);
- * its contents are rebuilt by every call.
+ * attention loop is a contiguous 1 KB wave read, and stores per page its
+ * softmax factors (scales, and a bound from its largest key norm that lets the
+ * softmax skip row maxima that cannot move); its contents are rebuilt by every
+ * call.
  * ------------------------------------------------------------------------- */
 size_t pw_union_attention_workspace_bytes(const pw_shape* shape, int32_t g);
 pw_status pw_union_attention(const pw_shape* shape, const uint16_t* Q,

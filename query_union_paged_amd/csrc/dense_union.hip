@@ -259,7 +259,7 @@ hipError_t launch_dense_union(const pw_shape& s, const uint16_t* Q, const uint8_
   float* partials = reinterpret_cast<float*>(base + d.off_part);
   const int G = s.H_q / s.H_kv;
   uint8_t* tiles = reinterpret_cast<uint8_t*>(base + d.off_tiles);
-  hipError_t e0 = tile_kv(s, K, V, tiles, stream);
+  hipError_t e0 = tile_kv(s, K, V, scales, tiles, stream);
   if (e0 != hipSuccess) return e0;
   const int n_map = s.H_kv * s.N_pages;
   if (pairs != nullptr) {

@@ -41,11 +41,12 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 // Host-side launchers (implemented next to their kernels).
 hipError_t launch_group(const pw_shape& s, const int32_t* sel, int W, int g, int32_t* ids,
                         hipStream_t stream);
-// FP8 K/V pages re-tiled in MFMA operand order (K tiles, then V tiles).
+// FP8 K/V pages re-tiled in MFMA operand order (K tiles, then V tiles), then
+// 16 bytes of softmax factors per (page, KV head).
 size_t tiled_kv_bytes(const pw_shape& s);
 // KV heads h_begin .. h_begin + h_count - 1 (h_count < 0: all heads)
-hipError_t tile_kv(const pw_shape& s, const uint8_t* K, const uint8_t* V, uint8_t* tiles,
-                   hipStream_t stream, int h_begin = 0, int h_count = -1);
+hipError_t tile_kv(const pw_shape& s, const uint8_t* K, const uint8_t* V, const float* scales,
+                   uint8_t* tiles, hipStream_t stream, int h_begin = 0, int h_count = -1);
 hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
                                   const uint8_t* V, const float* scales, const int32_t* sel,
                                   const int32_t* ids, int g, int h_begin, int h_count,

@@ -59,7 +59,8 @@ struct UAParams {
   const uint8_t* Kt;   // tiled copies of the FP8 K and V pages (see tile_kv_kernel)
   const uint8_t* Vt;
   const float* scales;
-  const float* kn;     // [N][Hkv]: largest key norm of each K page, in code units
+  const float4* pf;    // [N][Hkv] page factors (tile_kv_kernel): k_scale * qk_scale,
+                       // score bound factor, log2(v_scale), 1 / v_scale
   const int32_t* sel;
   const int32_t* ids;
   uint16_t* O;
@@ -126,16 +127,20 @@ __device__ __forceinline__ uint4 load16(const uint8_t* p) {
 // at byte 16 * ((kt * D/32 + c) * 64 + l), resp. 16 * ((2 dt + j) * 64 + l);
 // key slots >= P are zero.  The attention loop then reads each page with
 // contiguous 1 KB wave loads instead of one 128-byte row per lane.
-// The same pass stores kn[u][h] = (1 + 2^-9) * max over the page's keys of the
-// Euclidean norm of the decoded e4m3 codes (no scale): with the norm of a query
-// row it bounds every score of that row on the page.
+// The same pass stores the page's uniform softmax factors pf[u][h] = {c, kn * |c|,
+// log2(v_scale), 1 / v_scale} with c = k_scale * log2(e) / sqrt(D) and kn =
+// (1 + 2^-9) * the largest Euclidean norm of the page's decoded e4m3 key codes:
+// kn * |c| times the norm of a query row bounds every score of that row on the
+// page (log2 units).  The attention loop then reads them with one scalar load.
 template <int D>
 __global__ __launch_bounds__(256) void tile_kv_kernel(const uint8_t* __restrict__ K,
                                                       const uint8_t* __restrict__ V,
+                                                      const float* __restrict__ scales,
+                                                      float qk_scale,
                                                       uint8_t* __restrict__ Kt,
                                                       uint8_t* __restrict__ Vt,
-                                                      float* __restrict__ kn, int P, int Hkv,
-                                                      int h_begin, int h_count) {
+                                                      float4* __restrict__ pf, int N, int P,
+                                                      int Hkv, int h_begin, int h_count) {
   constexpr int KCH = D / 32, DT = D / 32;
   // one block per (page, head) of heads h_begin .. h_begin + h_count - 1
   const size_t blk = (size_t)(blockIdx.x / h_count) * Hkv + h_begin + blockIdx.x % h_count;
@@ -183,8 +188,12 @@ __global__ __launch_bounds__(256) void tile_kv_kernel(const uint8_t* __restrict_
   for (int o = 4; o < 64; o <<= 1) ss = fmaxf(ss, __shfl_xor(ss, o));
   if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = ss;
   __syncthreads();
-  if (threadIdx.x == 0)
-    kn[blk] = sqrtf(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))) * kNormSlack;
+  if (threadIdx.x == 0) {
+    const float kn = sqrtf(fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]))) * kNormSlack;
+    const float c = scales[blk] * qk_scale;
+    const float vs = scales[(size_t)N * Hkv + blk];
+    pf[blk] = make_float4(c, kn * fabsf(c), __builtin_amdgcn_logf(vs), __builtin_amdgcn_rcpf(vs));
+  }
 }
 
 // MODE kUnionMode: groups of query IDs, union of their selected pages, O out.
@@ -407,7 +416,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   // below is one contiguous 1 KB read of the wave (lane l at 16 * l).
   uint4 kbuf[2][KCH], vbuf[DT][2];
   f32x16 sacc[NT][2];
-  float ksr = 0.f, vsr = 0.f, knr = 0.f;
+  float4 pfr = make_float4(0.f, 0.f, 0.f, 0.f);
   auto page_of = [&](int i) {       // wave-uniform
     return __builtin_amdgcn_readfirstlane((int)(list[min(i, n_u - 1)] & 0xFFFF));
   };
@@ -438,9 +447,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
         vr[dt][j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                   vrs, loff, so + 1024 * (2 * dt + j), 0));
   };
-  const float* kscale = p.scales + h;                       // [N][Hkv]
-  const float* vscale = p.scales + (size_t)p.N * p.Hkv + h;
-  const float* knorm = p.kn + h;                            // [N][Hkv]
+  const float4* pfac = p.pf + h;                            // [N][Hkv]
   // S^T = K (Qhi + Qlo)^T on the FP8 MFMA
   auto qk = [&](const uint4 (&kr)[2][KCH], f32x16 (&sc)[NT][2]) {
 #pragma unroll
@@ -488,12 +495,11 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   // online softmax in the log2 domain, v_scale folded into the exponent; the
   // probabilities are produced as bf16 MFMA operands; returns the rescale
   // factor of the accumulator (1 unless the reference max moved)
-  auto softmax = [&](f32x16 (&sc)[NT][2], uint32_t mbits, float ks_raw, float vs_raw,
-                     float kn_raw, bf16x8 (&pB)[NT][4], float (&alph)[NT]) {
-    const float ksc0 = ks_raw * p.qk_scale;
-    const float kb0 = kn_raw * fabsf(ksc0);
-    const float lvs = __builtin_amdgcn_logf(vs_raw);    // log2
-    const float ivs = __builtin_amdgcn_rcpf(vs_raw);
+  auto softmax = [&](f32x16 (&sc)[NT][2], uint32_t mbits, const float4 f,
+                     bf16x8 (&pB)[NT][4], float (&alph)[NT]) {
+    const float ksc0 = f.x, kb0 = f.y;
+    const float lvs = f.z;    // log2(v_scale)
+    const float ivs = f.w;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const bool member = slot[nt] >= 0 && ((mbits >> slot[nt]) & 1u);
@@ -573,23 +579,19 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
     const int u0 = page_of(0);
     load_k(kbuf, u0);
     load_v(vbuf, u0);
-    ksr = kscale[(size_t)u0 * p.Hkv];
-    vsr = vscale[(size_t)u0 * p.Hkv];
-    knr = knorm[(size_t)u0 * p.Hkv];
+    pfr = pfac[(size_t)u0 * p.Hkv];
   }
   bf16x8 pB[NT][4];
   float alph[NT];
   for (int up = 0; up < n_u; ++up) {
     const uint32_t ent = __builtin_amdgcn_readfirstlane(list[up]);
-    const float ks_c = ksr, vs_c = vsr, kn_c = knr;
+    const float4 pf_c = pfr;
     const int u1 = page_of(up + 1);
     qk(kbuf, sacc);
     load_k(kbuf, u1);                     // K registers are free once the MFMAs have read them
-    ksr = kscale[(size_t)u1 * p.Hkv];
-    vsr = vscale[(size_t)u1 * p.Hkv];
-    knr = knorm[(size_t)u1 * p.Hkv];
+    pfr = pfac[(size_t)u1 * p.Hkv];
     mask_page(sacc, ent & 0xFFFF);
-    softmax(sacc, ent >> 16, ks_c, vs_c, kn_c, pB, alph);
+    softmax(sacc, ent >> 16, pf_c, pB, alph);
     rescale(alph);
     pv(vbuf, pB);
     load_v(vbuf, u1);
@@ -658,25 +660,26 @@ void common_params(UAParams& prm, const pw_shape& s, const uint16_t* Q, const fl
 
 }  // namespace
 
-// Workspace of the re-tiled pages: K tiles, V tiles, then the page key norms.
-size_t tiled_kn_offset(const pw_shape& s) { return (size_t)2 * s.N_pages * s.H_kv * 64 * s.D; }
+// Workspace of the re-tiled pages: K tiles, V tiles, then the page factors.
+size_t tiled_pf_offset(const pw_shape& s) { return (size_t)2 * s.N_pages * s.H_kv * 64 * s.D; }
 size_t tiled_kv_bytes(const pw_shape& s) {
-  return tiled_kn_offset(s) + ((size_t)4 * s.N_pages * s.H_kv + 255) / 256 * 256;
+  return tiled_pf_offset(s) + ((size_t)16 * s.N_pages * s.H_kv + 255) / 256 * 256;
 }
 
-hipError_t tile_kv(const pw_shape& s, const uint8_t* K, const uint8_t* V, uint8_t* tiles,
-                   hipStream_t stream, int h_begin, int h_count) {
+hipError_t tile_kv(const pw_shape& s, const uint8_t* K, const uint8_t* V, const float* scales,
+                   uint8_t* tiles, hipStream_t stream, int h_begin, int h_count) {
   if (h_count < 0) h_count = s.H_kv;
   uint8_t* Kt = tiles;
-  uint8_t* Vt = tiles + tiled_kn_offset(s) / 2;
-  float* kn = reinterpret_cast<float*>(tiles + tiled_kn_offset(s));
+  uint8_t* Vt = tiles + tiled_pf_offset(s) / 2;
+  float4* pf = reinterpret_cast<float4*>(tiles + tiled_pf_offset(s));
+  const float qk_scale = kLog2e / sqrtf((float)s.D);
   const dim3 grid(s.N_pages * h_count);
   if (s.D == 128)
-    hipLaunchKernelGGL(tile_kv_kernel<128>, grid, dim3(256), 0, stream, K, V, Kt, Vt, kn, s.P,
-                       s.H_kv, h_begin, h_count);
+    hipLaunchKernelGGL(tile_kv_kernel<128>, grid, dim3(256), 0, stream, K, V, scales, qk_scale,
+                       Kt, Vt, pf, s.N_pages, s.P, s.H_kv, h_begin, h_count);
   else
-    hipLaunchKernelGGL(tile_kv_kernel<64>, grid, dim3(256), 0, stream, K, V, Kt, Vt, kn, s.P,
-                       s.H_kv, h_begin, h_count);
+    hipLaunchKernelGGL(tile_kv_kernel<64>, grid, dim3(256), 0, stream, K, V, scales, qk_scale,
+                       Kt, Vt, pf, s.N_pages, s.P, s.H_kv, h_begin, h_count);
   return hipGetLastError();
 }
 
@@ -685,13 +688,13 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
                                   const int32_t* ids, int g, int h_begin, int h_count,
                                   uint16_t* O, void* ws, hipStream_t stream) {
   uint8_t* tiles = static_cast<uint8_t*>(ws);
-  hipError_t e = tile_kv(s, K, V, tiles, stream, h_begin, h_count);
+  hipError_t e = tile_kv(s, K, V, scales, tiles, stream, h_begin, h_count);
   if (e != hipSuccess) return e;
   UAParams prm;
   common_params(prm, s, Q, scales);
   prm.Kt = tiles;
-  prm.Vt = tiles + tiled_kn_offset(s) / 2;
-  prm.kn = reinterpret_cast<const float*>(tiles + tiled_kn_offset(s));
+  prm.Vt = tiles + tiled_pf_offset(s) / 2;
+  prm.pf = reinterpret_cast<const float4*>(tiles + tiled_pf_offset(s));
   prm.sel = sel; prm.ids = ids; prm.O = O; prm.g = g;
   prm.groups_per_head = (s.T + g - 1) / g;
   prm.total_groups = prm.groups_per_head * h_count;
@@ -714,8 +717,8 @@ hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uin
   UAParams prm;
   common_params(prm, s, Q, scales);
   prm.Kt = tiles;
-  prm.Vt = tiles + tiled_kn_offset(s) / 2;
-  prm.kn = reinterpret_cast<const float*>(tiles + tiled_kn_offset(s));
+  prm.Vt = tiles + tiled_pf_offset(s) / 2;
+  prm.pf = reinterpret_cast<const float4*>(tiles + tiled_pf_offset(s));
   prm.plist = plist; prm.pcount = pcount; prm.partials = partials;
   prm.tstart = tstart; prm.pairs = pairs; prm.tiles_head = tiles_head;
   prm.Np = Np; prm.Tc = Tc; prm.t0 = t0;

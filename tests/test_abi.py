@@ -75,7 +75,7 @@ def test_attention_validation():
     assert _attn(_shape(S=-1)) == pw.PW_ERR_DIMS
     shp = _shape()
     need = pw._lib.pw_union_attention_workspace_bytes(ctypes.byref(shp), 8)
-    assert need == 2 * 64 * 1 * 64 * 64 + 256      # K and V tiles, then 64 page key norms
+    assert need == 2 * 64 * 1 * 64 * 64 + 1024     # K and V tiles, then 16 bytes per page
     f = pw._lib.pw_union_attention
     assert f(ctypes.byref(shp), *[FAKE] * 6, 8, FAKE, None, need, None) == pw.PW_ERR_NULL
     assert f(ctypes.byref(shp), *[FAKE] * 6, 8, FAKE, FAKE, need - 1, None) == pw.PW_ERR_WORKSPACE
