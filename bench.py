@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_64k")
     ap.add_argument("--no-arms", action="store_true", help="skip the identity / g=1 comparison arms")
+    ap.add_argument("--only-arm", choices=["selector"], default=None,
+                    help="run only this comparison arm (for profiling it)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle sample time")
     ap.add_argument("--cold", type=int, default=5, help="cold-cache runs (MALL/L2 flushed)")
@@ -374,7 +376,9 @@ def main():
                                "peak_GBs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS}}
 
     arms = {}
-    if not args.no_arms:
+    if args.only_arm == "selector":
+        arms["selector"] = selector_arm(pw, torch, wl, dev, shp, O, ws)
+    elif not args.no_arms:
         ident = torch.arange(wl.T, dtype=torch.int32, device="cuda").repeat(wl.H_kv, 1).contiguous()
         for name, g_arm, ids_arm in [("identity_union8", wl.g, ident), ("per_query_g1", 1, ident)]:
             n = 5 if g_arm == 1 else 10

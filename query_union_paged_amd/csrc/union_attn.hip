@@ -216,9 +216,12 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber them so
   // each XCD sweeps a contiguous range of groups (one KV head's pages stay in
   // that XCD's L2).
+  // Each XCD takes its range from the top down: late queries have the largest
+  // supports, so the cheap early groups are the ones left for the tail.
   const int nb = gridDim.x, b = blockIdx.x;
   const int xcd = b & 7, per = nb >> 3, extra = nb & 7;
-  const int lb = xcd * per + min(xcd, extra) + (b >> 3);
+  const int cnt = per + (xcd < extra ? 1 : 0);       // workgroups of this XCD
+  const int lb = xcd * per + min(xcd, extra) + (cnt - 1 - (b >> 3));
   const int wid = lb * PW_UA_WG_WAVES + wave;
   if (wid >= p.total_items) return;
   const int rt = wid % p.n_rt;              // which 32-row tile of the group
