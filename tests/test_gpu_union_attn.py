@@ -297,6 +297,34 @@ def test_moving_reference_maximum():
     assert torch.equal(O.view(torch.int16), O_1.view(torch.int16))
 
 
+def test_tight_score_bound():
+    # every Q row is a power-of-two multiple of one key of a page it selected, so that page's
+    # best score equals |q| * max |k| (the norm bound is tight, up to rounding); the rows reach
+    # logits of several tens, so the bound decides between skipping and computing row maxima
+    # right at the lazy threshold
+    log("[case] union tight score bound")
+    T, P, Hq, Hkv, D, S = 512, 16, 4, 1, 128, 8
+    inp = tiny_problem(T=T, Hq=Hq, Hkv=Hkv, D=D, P=P, S=S, seed=95)
+    rng = np.random.default_rng(7)
+    kdec = torch.from_numpy(inp["k_codes"]).view(torch.float8_e4m3fn).float().numpy()
+    sel = inp["sel_pages"]
+    q = np.zeros((T, Hq, D), np.float32)
+    for t in range(T):
+        pages = sel[0, t][(sel[0, t] >= 0) & (sel[0, t] * P <= t)]
+        for j in range(Hq):
+            u = int(rng.choice(pages))
+            c = int(rng.integers(0, min(P, t - u * P + 1)))
+            q[t, j] = kdec[u, 0, c] * 2.0 ** int(rng.integers(-2, 3))
+    qb = torch.from_numpy(q).to(torch.bfloat16)
+    assert torch.equal(qb.float(), torch.from_numpy(q))          # exact in bf16
+    inp = dict(inp, q_bits=qb.view(torch.int16).numpy().view(np.uint16))
+    O, _ = _run(inp, 8, "regroup", 64)
+    pairs = _all_pairs(Hkv, T)
+    assert_close(gpu_rows(O, pairs, Hq // Hkv), oracle_rows(inp, pairs), "tight score bound")
+    O_id, _ = _run(inp, 8, "identity")
+    assert torch.equal(O.view(torch.int16), O_id.view(torch.int16))
+
+
 @pytest.mark.parametrize("T,P,g,W", [(16, 16, 16, 16), (16, 16, 8, 16), (32, 16, 1, 32), (64, 64, 4, 64)])
 def test_minimal_shapes(T, P, g, W):
     # one or two pages, a window equal to the sequence, groups of one or of the whole sequence
