@@ -1,13 +1,19 @@
 """Complete-call benchmark of query-union sparse-attention prefill on one MI355X.
 
 One step = one complete call on resident inputs: the grouping search
-(pw_group) followed by the union attention (pw_union_attention), both on the
-same stream.  Default workload: 64K-token prefill of a Llama-3-8B-like layer
+(pw_group), the re-tiling of the FP8 pages (pw_tile_kv) and the union attention
+(pw_union_attention_tiled), all on one stream, each bracketed by HIP events.
+Every timed step is cold: a 1 GiB buffer is written before it (outside its
+events), which evicts the MALL and the L2.  Warm steps (no flush) are reported
+beside it.  Default workload: 64K-token prefill of a Llama-3-8B-like layer
 (32 Q / 8 KV heads, d = 128, page 64, 64 selected pages per (query, KV head),
 Zipf(1.1) community draws, W = 256, g = 8), FP8 e4m3fn KV, bf16 Q and O.
 
-Prints one JSON line (rank 0).  `value` is useful TFLOP/s: 4*D flops per
-(visible selected key, Q head), i.e. only each query's own support.
+Prints one JSON line.  `value` is useful TFLOP/s of the cold complete call:
+4*D flops per (visible selected key, Q head), i.e. only each query's own
+support.  `roofline` is for the dominant kernel (the union attention): the same
+useful flops over its mean duration in the timed steps, against the 2.5 PFLOP/s
+dense bf16 peak.
 """
 from __future__ import annotations
 
@@ -41,7 +47,6 @@ def parse():
                     help="run only this comparison arm (for profiling it)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle sample time")
-    ap.add_argument("--cold", type=int, default=5, help="cold-cache runs (MALL/L2 flushed)")
     ap.add_argument("--gen-workers", type=int, default=16,
                     help="processes for input generation (0: in-process, e.g. under a profiler)")
     ap.add_argument("--sweep", action="store_true",
@@ -91,22 +96,29 @@ def pair_entries(sel: np.ndarray, pairs, N: int) -> float:
     return tot / (H * T)
 
 
+KERNEL_FILES = ("query_union_paged_amd/csrc/union_attn.hip", "query_union_paged_amd/csrc/pw_internal.h",
+                "query_union_paged_amd/build.py")
+
+
 def kernel_hash() -> str:
-    src = os.path.join(ROOT, "query_union_paged_amd", "csrc", "union_attn.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    """Hash of the attention kernel's source, its shared header and the build flags."""
+    h = hashlib.sha256()
+    for f in KERNEL_FILES:
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
-def recorded_traffic():
-    """HBM bytes of one pw_union_attention call (re-tiling + attention kernels), from the
-    rocprofv3 FETCH_SIZE / WRITE_SIZE passes stored under profiles/, each scaled by what the
-    same counter reads for a plain 1 GiB copy; None unless taken on this kernel source."""
+def recorded_traffic(workload: str):
+    """DRAM bytes of one union_attn_kernel launch, from the rocprofv3 FETCH_SIZE / WRITE_SIZE
+    passes stored under profiles/, each scaled by what the same counter reads for a plain
+    1 GiB copy; None unless taken on this kernel source and build flags."""
     path = os.path.join(ROOT, "profiles", "union_attn_counters.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_sha256_16") != kernel_hash():
+    if rec.get("kernel_sha256_16") != kernel_hash() or rec.get("workload") != workload:
         return None
-    return rec.get("hbm_bytes_per_call")
+    return rec.get("dram_bytes_per_launch")
 
 
 def cpu_baseline(inp, wl, seconds: float):
@@ -227,40 +239,27 @@ def head_pipeline_arm(pw, torch, wl, dev, shp, O, ws, reps: int = 10):
     return out
 
 
-def selector_arm(pw, torch, wl, dev, shp, O, ws, reps: int = 5):
+def selector_arm(pw, torch, wl, dev, shp, O, ws, ident, cold_ms):
     """The synthetic GPU selector (sink + 2 local pages + top pages by block key sums) and the
-    complete call on its selections, regrouped and with identity grouping."""
-    stream = torch.cuda.current_stream()
+    complete call on its selections, regrouped and with identity grouping (cold calls)."""
     sws = torch.empty(pw.pw_select_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
     sel = torch.empty_like(dev["sel_pages"])
     ids = torch.empty((wl.H_kv, wl.T), dtype=torch.int32, device="cuda")
-    ident = torch.arange(wl.T, dtype=torch.int32, device="cuda").repeat(wl.H_kv, 1).contiguous()
-
-    def timed(fn):
-        fn()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(reps):
-            fn()
-        b.record(stream)
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / reps
-
-    def attn(idv):
-        return lambda: pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"],
-                                             dev["scales"], sel, idv, wl.g, O=O, workspace=ws)
-    sel_ms = timed(lambda: pw.pw_select(shp, dev["q_bits"], dev["k_codes"], dev["scales"], 2,
-                                        sel_pages=sel, workspace=sws))
-    search_ms = timed(lambda: pw.pw_group(shp, sel, wl.W, wl.g, query_ids=ids))
-    attn_ms = timed(attn(ids))
-    ident_ms = timed(attn(ident))
+    q, k, v, sc = dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"]
+    select = lambda: pw.pw_select(shp, q, k, sc, 2, sel_pages=sel, workspace=sws)
+    search = lambda: pw.pw_group(shp, sel, wl.W, wl.g, query_ids=ids)
+    tile = lambda: pw.pw_tile_kv(shp, k, v, sc, workspace=ws)
+    attn = lambda idv: (lambda: pw.pw_union_attention_tiled(shp, q, sel, idv, wl.g, ws, O=O))
+    sel_ms = cold_ms([select])
+    select()
+    call_ms = cold_ms([search, tile, attn(ids)])
+    ident_ms = cold_ms([tile, attn(ident)])
     sel_np = sel.cpu().numpy()
     u = union_stats(sel_np, ids.cpu().numpy(), wl.g, wl.N)
     ui = union_stats(sel_np, ident.cpu().numpy(), wl.g, wl.N)
     del sws
-    return {"select_ms": sel_ms, "search_ms": search_ms, "attention_ms": attn_ms,
-            "call_ms": search_ms + attn_ms, "identity_attention_ms": ident_ms,
-            "regroup_gain_vs_identity": ident_ms / (search_ms + attn_ms),
+    return {"select_ms": sel_ms, "call_ms": call_ms, "identity_call_ms": ident_ms,
+            "regroup_gain_vs_identity": ident_ms / call_ms,
             "union_pages_mean": float(u.mean()), "identity_union_pages_mean": float(ui.mean()),
             "n_local": 2}
 
@@ -273,6 +272,32 @@ def cpu_model() -> str:
     except OSError:
         pass
     return "unknown"
+
+
+class Calls:
+    """Cold and warm timing of device calls on one stream.  A cold call is preceded by a
+    1 GiB write (outside its events) that evicts the MALL and the L2."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+        self.flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+
+    def run(self, stages, n: int, cold: bool):
+        """stages: list of callables run back to back; returns [n][len(stages)] ms."""
+        torch = self.torch
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(stages) + 1)]
+              for _ in range(n)]
+        for row in ev:
+            if cold:
+                self.flush.fill_(1.0)
+            row[0].record(self.stream)
+            for fn, e in zip(stages, row[1:]):
+                fn()
+                e.record(self.stream)
+        torch.cuda.synchronize()
+        return np.array([[row[i].elapsed_time(row[i + 1]) for i in range(len(stages))]
+                         for row in ev])
 
 
 def main():
@@ -294,40 +319,33 @@ def main():
     log(f"[bench] inputs {wl.name} generated in {time.time() - t0:.1f}s")
     dev = pw.to_device(inp)
     shp = pw.shape(*wl.shape_tuple())
-    stream = torch.cuda.current_stream()
     F_u = synth.useful_flops(inp["sel_pages"], wl)
 
     ids = pw.pw_group(shp, dev["sel_pages"], wl.W, wl.g)
     ws = torch.empty(pw.pw_union_attention_workspace_bytes(shp, wl.g), dtype=torch.uint8,
                      device="cuda")
-    O = pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
-                              dev["sel_pages"], ids, wl.g, workspace=ws)
-    torch.cuda.synchronize()
+    O = torch.empty((wl.T, wl.H_q, wl.D), dtype=torch.bfloat16, device="cuda")
+    q, k, v, sc, sel = dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"], dev["sel_pages"]
 
-    def step():
-        pw.pw_group(shp, dev["sel_pages"], wl.W, wl.g, query_ids=ids)
-        pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
-                              dev["sel_pages"], ids, wl.g, O=O, workspace=ws)
+    def search(sel_=sel, ids_=ids, W=wl.W, g=wl.g):
+        return lambda: pw.pw_group(shp, sel_, W, g, query_ids=ids_)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
-           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    tile = lambda: pw.pw_tile_kv(shp, k, v, sc, workspace=ws)
+
+    def attend(ids_=ids, g=wl.g, sel_=sel):
+        return lambda: pw.pw_union_attention_tiled(shp, q, sel_, ids_, g, ws, O=O)
+
+    stages = [search(), tile, attend()]
+    calls = Calls(torch)
+    calls.run(stages, args.warmup, cold=False)           # untimed warm-up
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for e0, e1, e2 in ev:
-        e0.record(stream)
-        pw.pw_group(shp, dev["sel_pages"], wl.W, wl.g, query_ids=ids)
-        e1.record(stream)
-        pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
-                              dev["sel_pages"], ids, wl.g, O=O, workspace=ws)
-        e2.record(stream)
-    torch.cuda.synchronize()
+    cold = calls.run(stages, args.steps, cold=True)       # the K timed steps (synchronised)
     wall = time.perf_counter() - t_start
-    search_ms = np.array([a.elapsed_time(b) for a, b, _ in ev])
-    attn_ms = np.array([b.elapsed_time(c) for _, b, c in ev])
-    ms_per_step = wall * 1e3 / args.steps
+    warm = calls.run(stages, args.steps, cold=False)
+    call_cold = cold.sum(axis=1)
+    call_warm = warm.sum(axis=1)
+    ms_per_step = float(np.median(call_cold))
     value = F_u / (ms_per_step * 1e-3) / 1e12
 
     if args.copy_calib:
@@ -338,105 +356,73 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # cold runs: a 1 GiB write between runs evicts MALL and L2
-    cold = []
-    if args.cold > 0:
-        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        for _ in range(args.cold):
-            flush.fill_(1.0)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            step()
-            b.record(stream)
-            torch.cuda.synchronize()
-            cold.append(a.elapsed_time(b))
-        del flush
-
-    # union accounting for the roofline (host-side, from the IDs the search returned)
+    # roofline of the dominant kernel (union_attn_kernel, launched by pw_union_attention_tiled)
     ids_np = ids.cpu().numpy()
     usz = union_stats(inp["sel_pages"], ids_np, wl.g, wl.N)
-    n_units = int(usz.sum())                       # (group, union page) pairs per launch
-    page_bytes = 2 * wl.P * wl.D                   # K + V e4m3fn bytes of one (page, KV head)
-    qo_bytes = 2 * wl.T * wl.H_q * wl.D * 2
-    meta_bytes = inp["sel_pages"].nbytes * 2 + ids_np.nbytes + inp["scales"].nbytes
-    alg_bytes = n_units * page_bytes + qo_bytes + meta_bytes
+    n_pages_total = int(usz.sum())                 # (group, union page) pairs per launch
     rows = wl.g * wl.G
-    flop_unit = 4 * ((rows + 31) // 32 * 32) * wl.P * wl.D   # QK^T + PV MFMA work per (group, page)
-    comp_flops = n_units * flop_unit
-    attn_avg_s = float(attn_ms.mean()) * 1e-3
-    mfma_tflops = comp_flops / attn_avg_s / 1e12
-    gbs = alg_bytes / attn_avg_s / 1e9
-    traffic = recorded_traffic()
-    roof = {"bound": "mfma", "achieved": mfma_tflops, "peak": BF16_MFMA_PEAK_TFLOPS,
-            "unit": "TFLOP/s", "frac": mfma_tflops / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic,
-            "kernel": "pw_union_attention call (tile_kv_kernel + union_attn_kernel)",
-            "flops_per_unit": flop_unit,
-            "units_per_launch": n_units,
-            "hbm_definition": {"algorithmic_bytes": alg_bytes, "achieved_GBs": gbs,
-                               "peak_GBs": HBM_PEAK_GBS, "frac": gbs / HBM_PEAK_GBS}}
+    comp_unit = 4 * ((rows + 31) // 32 * 32) * wl.P * wl.D   # MFMA flops per (group, page)
+    comp_flops = n_pages_total * comp_unit
+    attn_s = float(cold[:, 2].mean()) * 1e-3
+    achieved = F_u / attn_s / 1e12
+    tiled_bytes = pw.pw_union_attention_workspace_bytes(shp, wl.g)
+    compulsory = (2 * wl.T * wl.H_q * wl.D * 2 + inp["sel_pages"].nbytes + ids_np.nbytes
+                  + tiled_bytes)                   # Q, O, selections, IDs, tiled K/V read once
+    traffic = recorded_traffic(wl.name)
+    roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic,
+            "kernel": "union_attn_kernel (pw_union_attention_tiled), mean of the timed cold steps",
+            "flops_per_unit": 4 * wl.D, "unit_def": "(visible selected key, Q head) pair",
+            "units_per_launch": F_u / (4 * wl.D), "kernel_ms": attn_s * 1e3,
+            "complete_call": {"achieved": value, "frac": value / BF16_MFMA_PEAK_TFLOPS,
+                              "ms": ms_per_step},
+            "computed_work": {"flops": comp_flops, "per_group_page": comp_unit,
+                              "group_pages": n_pages_total,
+                              "achieved": comp_flops / attn_s / 1e12,
+                              "frac": comp_flops / attn_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+                              "useful_over_computed": F_u / comp_flops},
+            "dram": {"compulsory_bytes": compulsory,
+                     "measured_bytes": traffic,
+                     "measured_over_compulsory": (traffic / compulsory) if traffic else None,
+                     "measured_GBs": (traffic / attn_s / 1e9) if traffic else None,
+                     "peak_GBs": HBM_PEAK_GBS}}
+
+    def cold_ms(stages_, n=5):
+        calls.run(stages_, 1, cold=False)
+        return float(np.median(calls.run(stages_, n, cold=True).sum(axis=1)))
 
     arms = {}
+    ident = torch.arange(wl.T, dtype=torch.int32, device="cuda").repeat(wl.H_kv, 1).contiguous()
     if args.only_arm == "selector":
-        arms["selector"] = selector_arm(pw, torch, wl, dev, shp, O, ws)
+        arms["selector"] = selector_arm(pw, torch, wl, dev, shp, O, ws, ident, cold_ms)
     elif not args.no_arms:
-        ident = torch.arange(wl.T, dtype=torch.int32, device="cuda").repeat(wl.H_kv, 1).contiguous()
-        for name, g_arm, ids_arm in [("identity_union8", wl.g, ident), ("per_query_g1", 1, ident)]:
-            n = 5 if g_arm == 1 else 10
-            for _ in range(2):
-                pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"],
-                                      dev["scales"], dev["sel_pages"], ids_arm, g_arm, O=O,
-                                      workspace=ws)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record(stream)
-            for _ in range(n):
-                pw.pw_union_attention(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"],
-                                      dev["scales"], dev["sel_pages"], ids_arm, g_arm, O=O,
-                                      workspace=ws)
-            b.record(stream)
-            torch.cuda.synchronize()
-            ms = a.elapsed_time(b) / n
-            us = union_stats(inp["sel_pages"], ids_arm.cpu().numpy(), g_arm, wl.N)
+        for name, g_arm in [("identity_union8", wl.g), ("per_query_g1", 1)]:
+            ms = cold_ms([tile, attend(ident, g_arm)], n=5 if g_arm == 1 else 10)
+            us = union_stats(inp["sel_pages"], ident.cpu().numpy(), g_arm, wl.N)
             arms[name] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12,
                           "union_pages_mean": float(us.mean()), "union_pages_total": int(us.sum())}
         arms["regroup_gain_vs_identity"] = arms["identity_union8"]["ms"] / ms_per_step
         # the direct KV-page union (design-study comparison)
         dws = torch.empty(pw.pw_dense_union_ref_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
-        pw.pw_dense_union_ref(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
-                              dev["sel_pages"], O=O, workspace=dws)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        for _ in range(2):
-            pw.pw_dense_union_ref(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
-                                  dev["sel_pages"], O=O, workspace=dws)
-        b.record(stream)
-        torch.cuda.synchronize()
-        ms = a.elapsed_time(b) / 2
+        dense = lambda: pw.pw_dense_union_ref(shp, q, k, v, sc, sel, O=O, workspace=dws)
+        ms = cold_ms([dense], n=2)
         arms["direct_page_union"] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12,
                                      "workspace_GiB": dws.numel() / 2 ** 30,
                                      "entries_per_query": pair_entries(inp["sel_pages"], None, wl.N)}
         # the same with affinity pairs (greedy co-selection matching on the device)
         pws = torch.empty(pw.pw_page_pairs_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
-        prs = pw.pw_page_pairs(shp, dev["sel_pages"], workspace=pws)
-        pw.pw_dense_union_ref(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
-                              dev["sel_pages"], O=O, workspace=dws, pairs=prs)
-        t = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-        t[0].record(stream)
-        for _ in range(2):
-            pw.pw_page_pairs(shp, dev["sel_pages"], pairs=prs, workspace=pws)
-        t[1].record(stream)
-        for _ in range(2):
-            pw.pw_dense_union_ref(shp, dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"],
-                                  dev["sel_pages"], O=O, workspace=dws, pairs=prs)
-        t[2].record(stream)
-        torch.cuda.synchronize()
-        pair_ms, du_ms = t[0].elapsed_time(t[1]) / 2, t[1].elapsed_time(t[2]) / 2
+        prs = pw.pw_page_pairs(shp, sel, workspace=pws)
+        pairing = lambda: pw.pw_page_pairs(shp, sel, pairs=prs, workspace=pws)
+        dense_p = lambda: pw.pw_dense_union_ref(shp, q, k, v, sc, sel, O=O, workspace=dws, pairs=prs)
+        calls.run([pairing, dense_p], 1, cold=False)
+        t = np.median(calls.run([pairing, dense_p], 2, cold=True), axis=0)
         arms["direct_page_union_affinity"] = {
-            "pairing_ms": pair_ms, "union_ms": du_ms, "ms": pair_ms + du_ms,
-            "useful_TFLOPs": F_u / ((pair_ms + du_ms) * 1e-3) / 1e12,
+            "pairing_ms": float(t[0]), "union_ms": float(t[1]), "ms": float(t.sum()),
+            "useful_TFLOPs": F_u / (float(t.sum()) * 1e-3) / 1e12,
             "entries_per_query": pair_entries(inp["sel_pages"], prs.cpu().numpy(), wl.N)}
-        log(f"[bench] direct page union: adjacent {ms:.2f} ms, affinity {pair_ms:.2f} + {du_ms:.2f} ms")
+        log(f"[bench] direct page union: adjacent {ms:.2f} ms, affinity {t[0]:.2f} + {t[1]:.2f} ms")
         del dws, pws
-        arms["selector"] = selector_arm(pw, torch, wl, dev, shp, O, ws)
+        arms["selector"] = selector_arm(pw, torch, wl, dev, shp, O, ws, ident, cold_ms)
         arms["head_pipeline"] = head_pipeline_arm(pw, torch, wl, dev, shp, O, ws)
 
     swp = sweep(pw, torch, wl, inp, dev, shp, O, ws) if args.sweep else None
@@ -447,6 +433,10 @@ def main():
         cpu = cpu_baseline(inp, wl, args.cpu_seconds)
         log(f"[bench] cpu baseline {time.time() - t0:.1f}s")
 
+    def stats(a):
+        return {"median": float(np.median(a)), "p90": float(np.percentile(a, 90)),
+                "mean": float(np.mean(a))}
+
     out = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_per_step, "higher_is_better": True,
@@ -454,12 +444,13 @@ def main():
         "data": "synthetic (seeded captures, Q/K/V ~ N(0,1), e4m3fn KV with per-page scales)",
         "config": {"workload": wl.name, "tokens": wl.T, "H_q": wl.H_q, "H_kv": wl.H_kv,
                    "head_dim": wl.D, "page": wl.P, "selected_pages": wl.S, "W": wl.W, "g": wl.g,
-                   "kv": "fp8_e4m3fn", "grouping": "regrouped"},
-        "latency_ms": {"complete_call": ms_per_step, "search_mean": float(search_ms.mean()),
-                       "attention_mean": float(attn_ms.mean()),
-                       "attention_median": float(np.median(attn_ms)),
-                       "attention_p90": float(np.percentile(attn_ms, 90)),
-                       "complete_call_cold_median": float(np.median(cold)) if cold else None},
+                   "kv": "fp8_e4m3fn", "grouping": "regrouped", "timing": "cold (MALL+L2 flushed)"},
+        "latency_ms": {"complete_call_cold": stats(call_cold), "complete_call_warm": stats(call_warm),
+                       "search_cold": stats(cold[:, 0]), "tile_kv_cold": stats(cold[:, 1]),
+                       "attention_cold": stats(cold[:, 2]), "search_warm": stats(warm[:, 0]),
+                       "tile_kv_warm": stats(warm[:, 1]), "attention_warm": stats(warm[:, 2]),
+                       "timed_region_wall_s": wall},
+        "warm_value": F_u / (float(np.median(call_warm)) * 1e-3) / 1e12,
         "useful_flops": F_u,
         "union": {"pages_mean": float(usz.mean()), "pages_max": int(usz.max()),
                   "efficiency_useful_over_computed": F_u / comp_flops},

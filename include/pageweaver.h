@@ -57,8 +57,8 @@
  *             group k of that head is entries [k*g, k*g + g).
  *   Q         bf16  [T][H_q][D]      (bit patterns as uint16).
  *   K_fp8     e4m3fn [N_pages][H_kv][P][D]   token-major pages.
- *   V_fp8     e4m3fn [N_pages][H_kv][D][P]   dim-major pages: the token,
- *             which PV contracts over, is the contiguous index.
+ *   V_fp8     e4m3fn [N_pages][H_kv][P][D]   token-major pages (same layout
+ *             as K).
  *   scales    fp32  [2][N_pages][H_kv]        K scale then V scale of each
  *             (page, KV head); the value of a code is e4m3fn(code) * scale.
  *             Scales must be positive and finite.
@@ -105,7 +105,11 @@ typedef struct pw_shape {
  * written window by window, group by group, members in insertion order.  The
  * result is unique, so it is bit-exact against any correct implementation.
  *
- * In : sel_pages (see layouts), W in [1, 1024], g in [1, 16].
+ * In : sel_pages (see layouts), W in [1, 1024], g in [1, 16], W a multiple
+ *      of g (otherwise PW_ERR_UNSUPPORTED: the attention reads groups as
+ *      fixed runs of g IDs, which would then straddle windows).  T need not be
+ *      a multiple of W: the last window is shorter, and its last group may
+ *      have fewer than g members.
  * Out: query_ids int32 [H_kv][T] (every entry written).
  * Support set: N_pages <= 1024.  Workspace: none (returns 0).
  * ------------------------------------------------------------------------- */
@@ -146,8 +150,19 @@ pw_status pw_check_ids(const pw_shape* shape, const int32_t* query_ids, int32_t*
  *   O[t][hq] = sum_j softmax_j(<Q[t][hq], Khat_j> / sqrt(D)) Vhat_j
  * over exactly the keys j of its own selected pages with j <= t
  * (Khat/Vhat = e4m3fn(code) * scale).  O[t][hq] = 0 when that key set is
- * empty.  Arithmetic: bf16 x bf16 products with fp32 accumulation (the e4m3fn
- * codes convert to bf16 exactly), fp32 online softmax, bf16 (RNE) output.
+ * empty.  Arithmetic:
+ *   - Q K^T on the FP8 matrix cores: the e4m3fn K codes as stored, times a
+ *     two-part e4m3fn split of each Q row (the row is scaled by a power of two
+ *     so that its largest magnitude lies in [128, 256), then hi = e4m3(q) and
+ *     lo = e4m3(q - hi)); hi + lo equals the bf16 value for every element of
+ *     magnitude >= 2^-2 after scaling (its last bit is then at least the
+ *     e4m3 subnormal spacing 2^-9), and differs from it by at most 2^-10 (half
+ *     that spacing) below, i.e. at most 2^-17 (7.6e-6) of the row's largest
+ *     magnitude; fp32 accumulation;
+ *   - fp32 online softmax;
+ *   - P V on the bf16 matrix cores: P rounded to bf16 (RNE), the V codes
+ *     converted to bf16 exactly; fp32 accumulation;
+ *   - bf16 (RNE) output.
  * The result of a row does not depend on which other queries share its group.
  *
  * In : Q, K_fp8, V_fp8, scales, sel_pages, query_ids (see layouts), g in
@@ -168,7 +183,8 @@ pw_status pw_check_ids(const pw_shape* shape, const int32_t* query_ids, int32_t*
  * attention loop is a contiguous 1 KB wave read, and stores per page its
  * softmax factors (scales, and a bound from its largest key norm that lets the
  * softmax skip row maxima that cannot move); its contents are rebuilt by every
- * call.
+ * call.  pw_union_attention is exactly pw_tile_kv followed by
+ * pw_union_attention_tiled on the same workspace and stream.
  * ------------------------------------------------------------------------- */
 size_t pw_union_attention_workspace_bytes(const pw_shape* shape, int32_t g);
 pw_status pw_union_attention(const pw_shape* shape, const uint16_t* Q,
@@ -176,6 +192,33 @@ pw_status pw_union_attention(const pw_shape* shape, const uint16_t* Q,
                              const float* scales, const int32_t* sel_pages,
                              const int32_t* query_ids, int32_t g, uint16_t* O,
                              void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pw_tile_kv / pw_union_attention_tiled -- the two halves of
+ * pw_union_attention.
+ *
+ * [abs]: the kernel loads each group's union of selected pages once; the
+ * pages are read in matrix-core operand order from a re-tiled copy of the
+ * cache.  pw_tile_kv writes that copy (and the per-page softmax factors) into
+ * the workspace; pw_union_attention_tiled runs the attention on it.  A caller
+ * that attends to the same K/V several times (other selections or IDs, other
+ * Q) re-tiles once; the split also lets a caller time the two kernels apart.
+ *
+ * pw_tile_kv     In : K_fp8, V_fp8, scales (layouts above).  Out: ws.
+ * pw_union_attention_tiled
+ *                In : Q, sel_pages, query_ids, g (as pw_union_attention) and a
+ *                     workspace that pw_tile_kv filled for the same shape, K,
+ *                     V and scales (stream-ordered before this call; the
+ *                     library cannot check its contents).  Out: O.
+ * Workspace (both): pw_union_attention_workspace_bytes() bytes, 256-byte
+ * aligned, required.  Support set and errors as pw_union_attention.
+ * ------------------------------------------------------------------------- */
+pw_status pw_tile_kv(const pw_shape* shape, const uint8_t* K_fp8, const uint8_t* V_fp8,
+                     const float* scales, void* ws, size_t ws_bytes, void* stream);
+pw_status pw_union_attention_tiled(const pw_shape* shape, const uint16_t* Q,
+                                   const int32_t* sel_pages, const int32_t* query_ids,
+                                   int32_t g, uint16_t* O, const void* ws, size_t ws_bytes,
+                                   void* stream);
 
 /* ---------------------------------------------------------------------------
  * pw_union_attention_heads -- pw_union_attention for KV heads
@@ -318,7 +361,7 @@ const char* pw_last_error(void);
 /* ABI version of this header, PW_ABI_VERSION. */
 int32_t pw_abi_version(void);
 
-#define PW_ABI_VERSION 1
+#define PW_ABI_VERSION 2
 
 #ifdef __cplusplus
 }

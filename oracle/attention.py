@@ -9,7 +9,7 @@ head h, query (token) t and Q head hq of h:
   support   S(h, t) = { u : u = sel[h][t][s] for some slot s, 0 <= u < N }
   keys      J = { u*P + c : u in S(h, t), 0 <= c < P, u*P + c <= t }
   K^(j)     = e4m3fn(K[u][h][c][:]) * k_scale[u][h]
-  V^(j)     = e4m3fn(V[u][h][:][c]) * v_scale[u][h]      (V page is dim-major)
+  V^(j)     = e4m3fn(V[u][h][c][:]) * v_scale[u][h]
   s_j       = <Q[t][hq], K^(j)> / sqrt(D)
   O[t][hq]  = sum_j softmax(s)_j V^(j)        (O = 0 when J is empty)
 
@@ -41,7 +41,7 @@ class Problem:
     def __init__(self, q_bits, k_codes, v_codes, scales, sel_pages):
         self.T, self.H_q, self.D = q_bits.shape
         self.N, self.H_kv, self.P, d2 = k_codes.shape
-        assert d2 == self.D and v_codes.shape == (self.N, self.H_kv, self.D, self.P)
+        assert d2 == self.D and v_codes.shape == (self.N, self.H_kv, self.P, self.D)
         assert scales.shape == (2, self.N, self.H_kv)
         assert sel_pages.shape[:2] == (self.H_kv, self.T)
         self.S = sel_pages.shape[2]
@@ -60,10 +60,9 @@ class Problem:
         return self._kd[h]
 
     def v_hat(self, h: int) -> np.ndarray:
-        """Dequantised V pages of KV head h, token-major: [N][P][D]."""
+        """Dequantised V pages of KV head h: [N][P][D]."""
         if h not in self._vd:
-            v = decode_e4m3fn(self.v_codes[:, h]) * self.scales[1, :, h, None, None]
-            self._vd[h] = np.ascontiguousarray(v.transpose(0, 2, 1))
+            self._vd[h] = decode_e4m3fn(self.v_codes[:, h]) * self.scales[1, :, h, None, None]
         return self._vd[h]
 
     @property

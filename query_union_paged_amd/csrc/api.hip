@@ -54,6 +54,18 @@ pw_status check_attention_support(const pw_shape* s, int g) {
   return PW_OK;
 }
 
+// The re-tiled K/V copy of pw_tile_kv: size, alignment, and the 2 GiB reach of
+// the 32-bit offsets its readers form.
+pw_status check_tiled_workspace(const pw_shape* s, const void* ws, size_t ws_bytes) {
+  const size_t need = pw::tiled_kv_bytes(*s);
+  if (!ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
+  if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (((uintptr_t)ws & 255) != 0) return fail(PW_ERR_DIMS, "workspace must be 256-byte aligned");
+  if (need / 2 > 0x7FFFFFFFu)
+    return fail(PW_ERR_UNSUPPORTED, "tiled K/V of %zu bytes exceeds 2 GiB", need / 2);
+  return PW_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -85,6 +97,9 @@ pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W, i
   if (!sel_pages || !query_ids) return fail(PW_ERR_NULL, "sel_pages and query_ids are required");
   if (W < 1 || W > 1024) return fail(PW_ERR_UNSUPPORTED, "W = %d outside [1, 1024]", W);
   if (g < 1 || g > 16) return fail(PW_ERR_UNSUPPORTED, "g = %d outside [1, 16]", g);
+  if (W % g != 0)
+    return fail(PW_ERR_UNSUPPORTED,
+                "W = %d is not a multiple of g = %d (attention groups would straddle windows)", W, g);
   if (shape->N_pages > 1024)
     return fail(PW_ERR_UNSUPPORTED, "N_pages = %d exceeds 1024 for the search", shape->N_pages);
   return hip_status(pw::launch_group(*shape, sel_pages, W, g, query_ids, (hipStream_t)stream),
@@ -128,12 +143,8 @@ static pw_status union_attention_range(const pw_shape* shape, const uint16_t* Q,
   if (h_begin < 0 || h_count < 1 || h_begin + h_count > shape->H_kv)
     return fail(PW_ERR_DIMS, "KV heads [%d, %d) outside [0, %d)", h_begin, h_begin + h_count,
                 shape->H_kv);
-  const size_t need = pw::tiled_kv_bytes(*shape);
-  if (!ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
-  if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
-  if (((uintptr_t)ws & 255) != 0) return fail(PW_ERR_DIMS, "workspace must be 256-byte aligned");
-  if (need / 2 > 0x7FFFFFFFu)
-    return fail(PW_ERR_UNSUPPORTED, "tiled K/V of %zu bytes exceeds 2 GiB", need / 2);
+  st = check_tiled_workspace(shape, ws, ws_bytes);
+  if (st != PW_OK) return st;
   return hip_status(pw::launch_union_attention(*shape, Q, K_fp8, V_fp8, scales, sel_pages,
                                                query_ids, g, h_begin, h_count, O, ws,
                                                (hipStream_t)stream),
@@ -159,6 +170,36 @@ pw_status pw_union_attention_heads(const pw_shape* shape, const uint16_t* Q,
                                h_count, O, ws, ws_bytes, stream, "pw_union_attention_heads launch");
 }
 
+pw_status pw_tile_kv(const pw_shape* shape, const uint8_t* K_fp8, const uint8_t* V_fp8,
+                     const float* scales, void* ws, size_t ws_bytes, void* stream) {
+  pw_status st = check_shape(shape);
+  if (st != PW_OK) return st;
+  if (!K_fp8 || !V_fp8 || !scales) return fail(PW_ERR_NULL, "K_fp8, V_fp8 and scales are required");
+  st = check_attention_support(shape, 1);
+  if (st != PW_OK) return st;
+  st = check_tiled_workspace(shape, ws, ws_bytes);
+  if (st != PW_OK) return st;
+  return hip_status(pw::tile_kv(*shape, K_fp8, V_fp8, scales, static_cast<uint8_t*>(ws),
+                                (hipStream_t)stream),
+                    "pw_tile_kv launch");
+}
+
+pw_status pw_union_attention_tiled(const pw_shape* shape, const uint16_t* Q,
+                                   const int32_t* sel_pages, const int32_t* query_ids, int32_t g,
+                                   uint16_t* O, const void* ws, size_t ws_bytes, void* stream) {
+  pw_status st = check_shape(shape);
+  if (st != PW_OK) return st;
+  if (!Q || !sel_pages || !query_ids || !O)
+    return fail(PW_ERR_NULL, "Q, sel_pages, query_ids and O are required");
+  st = check_attention_support(shape, g);
+  if (st != PW_OK) return st;
+  st = check_tiled_workspace(shape, ws, ws_bytes);
+  if (st != PW_OK) return st;
+  return hip_status(pw::launch_union_attention_tiled(*shape, Q, sel_pages, query_ids, g, 0,
+                                                     shape->H_kv, O, ws, (hipStream_t)stream),
+                    "pw_union_attention_tiled launch");
+}
+
 size_t pw_dense_union_ref_workspace_bytes(const pw_shape* shape) {
   if (check_shape(shape) != PW_OK) return 0;
   return pw::dense_union_workspace(*shape);
@@ -177,6 +218,9 @@ pw_status pw_dense_union_ref(const pw_shape* shape, const uint16_t* Q, const uin
     return fail(PW_ERR_UNSUPPORTED, "G = %d exceeds 8 for the page-pair tiles", shape->H_q / shape->H_kv);
   if (shape->N_pages > 4096)
     return fail(PW_ERR_UNSUPPORTED, "N_pages = %d exceeds 4096 for the page-pair lists", shape->N_pages);
+  if (pw::tiled_kv_bytes(*shape) / 2 > 0x7FFFFFFFu)
+    return fail(PW_ERR_UNSUPPORTED, "tiled K/V of %zu bytes exceeds 2 GiB",
+                pw::tiled_kv_bytes(*shape) / 2);
   const size_t need = pw::dense_union_workspace(*shape);
   if (need > 0 && !ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
   if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -200,6 +244,9 @@ pw_status pw_dense_union_paired(const pw_shape* shape, const uint16_t* Q, const 
     return fail(PW_ERR_UNSUPPORTED, "G = %d exceeds 8 for the page-pair tiles", shape->H_q / shape->H_kv);
   if (shape->N_pages > 2048)
     return fail(PW_ERR_UNSUPPORTED, "N_pages = %d exceeds 2048 for a pair table", shape->N_pages);
+  if (pw::tiled_kv_bytes(*shape) / 2 > 0x7FFFFFFFu)
+    return fail(PW_ERR_UNSUPPORTED, "tiled K/V of %zu bytes exceeds 2 GiB",
+                pw::tiled_kv_bytes(*shape) / 2);
   const size_t need = pw::dense_union_workspace(*shape);
   if (!ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
   if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);

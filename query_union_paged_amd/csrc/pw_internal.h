@@ -51,6 +51,11 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
                                   const uint8_t* V, const float* scales, const int32_t* sel,
                                   const int32_t* ids, int g, int h_begin, int h_count,
                                   uint16_t* O, void* ws, hipStream_t stream);
+// The attention alone, on a workspace that tile_kv has filled for heads
+// h_begin .. h_begin + h_count - 1.
+hipError_t launch_union_attention_tiled(const pw_shape& s, const uint16_t* Q, const int32_t* sel,
+                                        const int32_t* ids, int g, int h_begin, int h_count,
+                                        uint16_t* O, const void* ws, hipStream_t stream);
 hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* tiles,
                                  const float* scales, const int2* plist, const int* pcount,
                                  const int* tstart, const int2* pairs, int tiles_head,

@@ -13,10 +13,12 @@
 // of pages in ascending page order; four waves share a workgroup only for
 // scheduling.  Per page (64 keys):
 //   S^T = K_page * Q^T     v_mfma_scale_f32_32x32x64_f8f6f4 on the e4m3 codes
-//                          and an exact two-part e4m3 split of each bf16 Q
-//                          row (hi + lo); keys are the MFMA rows and query rows
-//                          the columns, so each lane holds one query row
-//                          (lane & 31) and 32 of its 64 keys;
+//                          and a two-part e4m3 split of each bf16 Q row
+//                          (hi + lo: exact for elements >= 2^-2 after the
+//                          row's power-of-two scaling, within 2^-10 below);
+//                          keys are the MFMA rows and query rows the columns,
+//                          so each lane holds one query row (lane & 31) and 32
+//                          of its 64 keys;
 //   online softmax         fp32 in registers, log2 domain, lazy rescale; row
 //                          max/sum finished with one cross-half lane swap; the
 //                          max pass is skipped when |q| * max |k| shows that no
@@ -24,11 +26,13 @@
 //   O^T += V_page^T * P^T  v_mfma_f32_32x32x16_bf16 with the V codes converted
 //                          to bf16 exactly; d is the MFMA row.
 // Page loads are contiguous 1 KB wave reads of the tiled copy straight into
-// operand registers (within a group each byte is used by one wave once, so LDS
-// staging would only add traffic); the per-page scales are folded into the
+// operand registers.  A group of at most 32 rows (G = 4, g = 8) is one wave,
+// which loads each union page once; a 64-row group (G = 8) is two waves, and
+// each of them loads every union page (the page's K/V bytes cross the vector
+// memory path twice per group).  The per-page scales are folded into the
 // scores (k) and into the exponent (v).  The key order inside the 32-row K
-// tiles is permuted so that the PV operands of every lane are 32 contiguous
-// tokens of a dim-major V page.
+// tiles is permuted so that the PV operands of every lane are 32 consecutive
+// keys of one d in the tiled V copy.
 //
 // Ownership.  A row whose query did not select a page gets p = 0 and its
 // running max untouched on that page (alpha = 1 exactly), so its result is
@@ -121,12 +125,16 @@ __device__ __forceinline__ uint4 load16(const uint8_t* p) {
 }
 
 // Re-tiles the FP8 pages of one layer into MFMA operand order (one workgroup
-// per (page, KV head) block of 64 key slots x D bytes, for K and for V):
+// per (page, KV head) block of 64 key slots x D bytes, for K and for V; both
+// cache pages are token-major [P][D]):
 //   K chunk (kt, c, l) = K[tile_key(l % 32, kt)][(D/2)(l/32) + 16c .. +16)
-//   V chunk (dt, j, l) = V[32 dt + l % 32][32 (l/32) + 16 j .. +16)   (dim-major page)
+//   V chunk (dt, j, l) = V[32 (l/32) + 16 j .. +16][32 dt + l % 32]   (16 keys of one d)
 // at byte 16 * ((kt * D/32 + c) * 64 + l), resp. 16 * ((2 dt + j) * 64 + l);
 // key slots >= P are zero.  The attention loop then reads each page with
-// contiguous 1 KB wave loads instead of one 128-byte row per lane.
+// contiguous 1 KB wave loads instead of one 128-byte row per lane.  A V chunk
+// gathers one column of the page: the page is staged in LDS and each thread
+// transposes 4 x 4 byte blocks (4 keys x 4 consecutive d) into 4 chunks of
+// consecutive lanes.
 // The same pass stores the page's uniform softmax factors pf[u][h] = {c, kn * |c|,
 // log2(v_scale), 1 / v_scale} with c = k_scale * log2(e) / sqrt(D) and kn =
 // (1 + 2^-9) * the largest Euclidean norm of the page's decoded e4m3 key codes:
@@ -142,12 +150,17 @@ __global__ __launch_bounds__(256) void tile_kv_kernel(const uint8_t* __restrict_
                                                       float4* __restrict__ pf, int N, int P,
                                                       int Hkv, int h_begin, int h_count) {
   constexpr int KCH = D / 32, DT = D / 32;
+  __shared__ uint4 vpage[64 * D / 16];        // the V page, 64 key rows (rows >= P zero)
   // one block per (page, head) of heads h_begin .. h_begin + h_count - 1
   const size_t blk = (size_t)(blockIdx.x / h_count) * Hkv + h_begin + blockIdx.x % h_count;
   const uint8_t* kp = K + blk * P * D;
-  const uint8_t* vp = V + blk * D * P;
+  const uint8_t* vp = V + blk * P * D;
   uint8_t* kt_out = Kt + blk * 64 * D;
   uint8_t* vt_out = Vt + blk * 64 * D;
+  for (int i = threadIdx.x; i < 64 * D / 16; i += blockDim.x) {
+    const int key = i / (D / 16);
+    vpage[i] = (key < P) ? load16(vp + 16 * (size_t)i) : make_uint4(0, 0, 0, 0);
+  }
   for (int q = threadIdx.x; q < 2 * KCH * 64; q += blockDim.x) {
     const int l = q & 63, kc = q >> 6, kt = kc / KCH, c = kc - kt * KCH;
     const int key = tile_key(l & 31, kt);
@@ -155,12 +168,28 @@ __global__ __launch_bounds__(256) void tile_kv_kernel(const uint8_t* __restrict_
                               : make_uint4(0, 0, 0, 0);
     *reinterpret_cast<uint4*>(kt_out + 16 * q) = v;
   }
-  for (int q = threadIdx.x; q < 2 * DT * 64; q += blockDim.x) {
-    const int l = q & 63, dj = q >> 6, dt = dj >> 1, j = dj & 1;
-    const int k0 = 32 * (l >> 5) + 16 * j;
-    const uint4 v = (k0 < P) ? load16(vp + (size_t)(32 * dt + (l & 31)) * P + k0)
-                             : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(vt_out + 16 * q) = v;
+  __syncthreads();
+  // V: work item (dt, j, l4) writes the chunks of lanes 4 l4 .. 4 l4 + 3 of
+  // chunk row 2 dt + j: d = d0 .. d0 + 3, keys k0 .. k0 + 15.
+  const uint32_t* vw = reinterpret_cast<const uint32_t*>(vpage);
+  for (int w = threadIdx.x; w < 2 * DT * 16; w += blockDim.x) {
+    const int l = 4 * (w & 15), dj = w >> 4, dt = dj >> 1, j = dj & 1;
+    const int d0 = 32 * dt + (l & 31), k0 = 32 * (l >> 5) + 16 * j;
+    uint32_t out[4][4];                       // out[i][kq]: d0 + i, keys k0 + 4 kq .. + 3
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      uint32_t r[4];                          // r[m]: bytes d0 .. d0 + 3 of key k0 + 4 kq + m
+#pragma unroll
+      for (int m = 0; m < 4; ++m) r[m] = vw[((k0 + 4 * kq + m) * D + d0) >> 2];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        out[i][kq] = ((r[0] >> (8 * i)) & 0xFFu) | (((r[1] >> (8 * i)) & 0xFFu) << 8) |
+                     (((r[2] >> (8 * i)) & 0xFFu) << 16) | (((r[3] >> (8 * i)) & 0xFFu) << 24);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<uint4*>(vt_out + 16 * ((2 * dt + j) * 64 + l + i)) =
+          make_uint4(out[i][0], out[i][1], out[i][2], out[i][3]);
   }
   // key norms: four threads per key slot, D / 4 codes each
   __shared__ float wmax[4];
@@ -340,9 +369,10 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
       (int)wave_min_u32(my_t >= 0 ? (uint32_t)my_t : 0xFFFFFFFFu));
 
   // ---- per-lane query rows and Q operands (B of S^T = K Q^T).  Each bf16 row
-  // is scaled by a power of two (absmax into [128, 256)) and split exactly into
-  // two e4m3fn parts, hi + lo, so that K^T can run on the FP8 MFMA straight
-  // from the cache bytes; 2^-e is folded back into the score scale.
+  // is scaled by a power of two (absmax into [128, 256)) and split into two
+  // e4m3fn parts, hi + lo (exact for elements >= 2^-2 after scaling, within
+  // 2^-10 below), so that K^T can run on the FP8 MFMA straight from the cache
+  // bytes; 2^-e is folded back into the score scale.
   constexpr int KQ = D / 64;     // fp8 MFMA k-steps (64 d each, 32 per lane half)
   int slot[NT], trow[NT], qhead[NT], pslot[NT];
   float rscale[NT], qn[NT];      // qn: bound on the norm of the row's hi + lo (scaled)
@@ -686,15 +716,12 @@ hipError_t tile_kv(const pw_shape& s, const uint8_t* K, const uint8_t* V, const 
   return hipGetLastError();
 }
 
-hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
-                                  const uint8_t* V, const float* scales, const int32_t* sel,
-                                  const int32_t* ids, int g, int h_begin, int h_count,
-                                  uint16_t* O, void* ws, hipStream_t stream) {
-  uint8_t* tiles = static_cast<uint8_t*>(ws);
-  hipError_t e = tile_kv(s, K, V, scales, tiles, stream, h_begin, h_count);
-  if (e != hipSuccess) return e;
+hipError_t launch_union_attention_tiled(const pw_shape& s, const uint16_t* Q, const int32_t* sel,
+                                        const int32_t* ids, int g, int h_begin, int h_count,
+                                        uint16_t* O, const void* ws, hipStream_t stream) {
+  const uint8_t* tiles = static_cast<const uint8_t*>(ws);
   UAParams prm;
-  common_params(prm, s, Q, scales);
+  common_params(prm, s, Q, nullptr);
   prm.Kt = tiles;
   prm.Vt = tiles + tiled_pf_offset(s) / 2;
   prm.pf = reinterpret_cast<const float4*>(tiles + tiled_pf_offset(s));
@@ -711,6 +738,15 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
   const size_t lds = (size_t)prm.lds_wave * PW_UA_WG_WAVES;
   return s.D == 128 ? launch_d<128, kUnionMode>(prm, blocks, lds, stream)
                     : launch_d<64, kUnionMode>(prm, blocks, lds, stream);
+}
+
+hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* K,
+                                  const uint8_t* V, const float* scales, const int32_t* sel,
+                                  const int32_t* ids, int g, int h_begin, int h_count,
+                                  uint16_t* O, void* ws, hipStream_t stream) {
+  hipError_t e = tile_kv(s, K, V, scales, static_cast<uint8_t*>(ws), stream, h_begin, h_count);
+  if (e != hipSuccess) return e;
+  return launch_union_attention_tiled(s, Q, sel, ids, g, h_begin, h_count, O, ws, stream);
 }
 
 hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* tiles,

@@ -50,6 +50,8 @@ _SIGS = {
     "pw_union_attention": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "pw_union_attention_heads": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp,
                                         _vp, _sz, _vp]),
+    "pw_tile_kv": (_i32, [_SHP, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "pw_union_attention_tiled": (_i32, [_SHP, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "pw_check_ids_workspace_bytes": (_sz, [_SHP]),
     "pw_check_ids": (_i32, [_SHP, _vp, _vp, _vp, _sz, _vp]),
     "pw_select_workspace_bytes": (_sz, [_SHP]),
@@ -133,7 +135,7 @@ def pw_union_attention(shp: PWShape, Q, K_fp8, V_fp8, scales, sel_pages, query_i
     T, Hq, Hkv, D, P, N, S = shp.T, shp.H_q, shp.H_kv, shp.D, shp.P, shp.N_pages, shp.S
     q = _dev(Q, "Q", _BF16, (T, Hq, D))
     k = _dev(K_fp8, "K_fp8", _U8, (N, Hkv, P, D))
-    v = _dev(V_fp8, "V_fp8", _U8, (N, Hkv, D, P))
+    v = _dev(V_fp8, "V_fp8", _U8, (N, Hkv, P, D))
     sc = _dev(scales, "scales", (torch.float32,), (2, N, Hkv))
     sel = _dev(sel_pages, "sel_pages", (torch.int32,), (Hkv, T, S))
     ids = _dev(query_ids, "query_ids", (torch.int32,), (Hkv, T))
@@ -152,6 +154,41 @@ def pw_union_attention(shp: PWShape, Q, K_fp8, V_fp8, scales, sel_pages, query_i
                                              int(heads[0]), int(heads[1]), o, ws,
                                              workspace.numel(), _stream(stream)),
                "pw_union_attention_heads")
+    return O
+
+
+def pw_tile_kv(shp: PWShape, K_fp8, V_fp8, scales, workspace: Optional[torch.Tensor] = None,
+               stream=None) -> torch.Tensor:
+    """Re-tile the FP8 K/V pages (and the per-page softmax factors) into a workspace for
+    pw_union_attention_tiled."""
+    N, Hkv, P, D = shp.N_pages, shp.H_kv, shp.P, shp.D
+    k = _dev(K_fp8, "K_fp8", _U8, (N, Hkv, P, D))
+    v = _dev(V_fp8, "V_fp8", _U8, (N, Hkv, P, D))
+    sc = _dev(scales, "scales", (torch.float32,), (2, N, Hkv))
+    if workspace is None:
+        workspace = torch.empty(pw_union_attention_workspace_bytes(shp), dtype=torch.uint8,
+                                device=K_fp8.device)
+    ws = _dev(workspace, "workspace", (torch.uint8,))
+    _check(_lib.pw_tile_kv(ctypes.byref(shp), k, v, sc, ws, workspace.numel(), _stream(stream)),
+           "pw_tile_kv")
+    return workspace
+
+
+def pw_union_attention_tiled(shp: PWShape, Q, sel_pages, query_ids, g: int,
+                             workspace: torch.Tensor, O: Optional[torch.Tensor] = None,
+                             stream=None) -> torch.Tensor:
+    """Union attention on a workspace that pw_tile_kv filled for the same K/V."""
+    T, Hq, Hkv, D, S = shp.T, shp.H_q, shp.H_kv, shp.D, shp.S
+    q = _dev(Q, "Q", _BF16, (T, Hq, D))
+    sel = _dev(sel_pages, "sel_pages", (torch.int32,), (Hkv, T, S))
+    ids = _dev(query_ids, "query_ids", (torch.int32,), (Hkv, T))
+    if O is None:
+        O = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=Q.device)
+    o = _dev(O, "O", _BF16, (T, Hq, D))
+    ws = _dev(workspace, "workspace", (torch.uint8,))
+    _check(_lib.pw_union_attention_tiled(ctypes.byref(shp), q, sel, ids, g, o, ws,
+                                         workspace.numel(), _stream(stream)),
+           "pw_union_attention_tiled")
     return O
 
 
@@ -233,7 +270,7 @@ def pw_dense_union_ref(shp: PWShape, Q, K_fp8, V_fp8, scales, sel_pages,
     T, Hq, Hkv, D, P, N, S = shp.T, shp.H_q, shp.H_kv, shp.D, shp.P, shp.N_pages, shp.S
     q = _dev(Q, "Q", _BF16, (T, Hq, D))
     k = _dev(K_fp8, "K_fp8", _U8, (N, Hkv, P, D))
-    v = _dev(V_fp8, "V_fp8", _U8, (N, Hkv, D, P))
+    v = _dev(V_fp8, "V_fp8", _U8, (N, Hkv, P, D))
     sc = _dev(scales, "scales", (torch.float32,), (2, N, Hkv))
     sel = _dev(sel_pages, "sel_pages", (torch.int32,), (Hkv, T, S))
     if O is None:

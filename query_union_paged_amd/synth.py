@@ -42,8 +42,7 @@ Layouts (the C-ABI layouts):
   sel_pages int32  [H_kv][T][S]
   q_bits    uint16 [T][H_q][D]        (bf16 bit patterns)
   k_codes   uint8  [N][H_kv][P][D]    (token-major page)
-  v_codes   uint8  [N][H_kv][D][P]    (dim-major page: the PV contraction
-                                       index, the token, is contiguous)
+  v_codes   uint8  [N][H_kv][P][D]    (token-major page)
   scales    fp32   [2][N][H_kv]       (K scales, then V scales)
 """
 from __future__ import annotations
@@ -223,7 +222,6 @@ def make_qkv(wl: Workload, variant: int = 0, peaked: bool = False):
     v = torch.randn((wl.N, wl.H_kv, wl.P, wl.D), generator=gen).to(torch.bfloat16)
     kc, ks = _quantise_blocks(k)
     vc, vs = _quantise_blocks(v)
-    vc = vc.transpose(2, 3).contiguous()            # [N][H][D][P]
     scales = torch.stack([ks, vs], dim=0).contiguous()
     return {
         "q_bits": q.view(torch.int16).numpy().view(np.uint16),

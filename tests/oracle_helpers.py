@@ -23,7 +23,7 @@ def tiny_problem(T=64, Hq=4, Hkv=2, D=16, P=16, S=4, seed=0, sel=None, q_scale=1
     return {
         "q_bits": q.view(torch.int16).numpy().view(np.uint16),
         "k_codes": k.view(torch.uint8).numpy(),
-        "v_codes": v.view(torch.uint8).numpy().transpose(0, 1, 3, 2).copy(),
+        "v_codes": v.view(torch.uint8).numpy(),
         "scales": scales,
         "sel_pages": sel,
     }
@@ -37,7 +37,7 @@ def torch_dense_reference(inp, allowed):
     G = Hq // Hkv
     q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).double()
     k = torch.from_numpy(kc).view(torch.float8_e4m3fn).double() * torch.from_numpy(sc[0]).double()[:, :, None, None]
-    v = torch.from_numpy(vc).view(torch.float8_e4m3fn).double().transpose(2, 3) * torch.from_numpy(sc[1]).double()[:, :, None, None]
+    v = torch.from_numpy(vc).view(torch.float8_e4m3fn).double() * torch.from_numpy(sc[1]).double()[:, :, None, None]
     k = k.permute(1, 0, 2, 3).reshape(Hkv, N * P, D)     # token j = u*P + c
     v = v.permute(1, 0, 2, 3).reshape(Hkv, N * P, D)
     kq = k.repeat_interleave(G, dim=0)                   # Q head hq -> KV head hq // G

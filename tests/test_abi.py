@@ -20,7 +20,7 @@ def test_every_declared_symbol_is_exported():
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     missing = [n for n in names if n not in exported]
     assert not missing, missing
-    assert pw._lib.pw_abi_version() == 1
+    assert pw._lib.pw_abi_version() == 2
 
 
 def test_status_strings():
@@ -55,6 +55,8 @@ def test_group_validation():
     assert _group(_shape(), W=0) == pw.PW_ERR_UNSUPPORTED
     assert _group(_shape(), W=1025) == pw.PW_ERR_UNSUPPORTED
     assert _group(_shape(), g=17) == pw.PW_ERR_UNSUPPORTED
+    assert _group(_shape(), W=36, g=8) == pw.PW_ERR_UNSUPPORTED      # W % g != 0
+    assert b"multiple of g" in pw._lib.pw_last_error()
     assert _group(_shape(T=2048 * 16, N_pages=2048)) == pw.PW_ERR_UNSUPPORTED
     assert b"W = 1025" in (_group(_shape(), W=1025) and pw._lib.pw_last_error())
     assert pw._lib.pw_group_workspace_bytes(ctypes.byref(_shape()), 32, 8) == 0
@@ -82,6 +84,28 @@ def test_attention_validation():
     assert f(ctypes.byref(shp), *[FAKE] * 6, 8, FAKE, ctypes.c_void_p(0x1010), need, None) == pw.PW_ERR_DIMS
 
 
+def test_tiled_validation():
+    shp = _shape()
+    need = pw._lib.pw_union_attention_workspace_bytes(ctypes.byref(shp), 8)
+    ws = ctypes.c_void_p(0x100000)
+    t = pw._lib.pw_tile_kv
+    assert t(None, FAKE, FAKE, FAKE, ws, need, None) == pw.PW_ERR_NULL
+    assert t(ctypes.byref(shp), None, FAKE, FAKE, ws, need, None) == pw.PW_ERR_NULL
+    assert t(ctypes.byref(shp), FAKE, FAKE, FAKE, None, need, None) == pw.PW_ERR_NULL
+    assert t(ctypes.byref(shp), FAKE, FAKE, FAKE, ws, need - 1, None) == pw.PW_ERR_WORKSPACE
+    assert t(ctypes.byref(shp), FAKE, FAKE, FAKE, ctypes.c_void_p(0x100010), need, None) == pw.PW_ERR_DIMS
+    assert t(ctypes.byref(_shape(D=96)), FAKE, FAKE, FAKE, ws, need, None) == pw.PW_ERR_UNSUPPORTED
+    a = pw._lib.pw_union_attention_tiled
+    assert a(ctypes.byref(shp), None, FAKE, FAKE, 8, FAKE, ws, need, None) == pw.PW_ERR_NULL
+    assert a(ctypes.byref(shp), FAKE, FAKE, FAKE, 8, None, ws, need, None) == pw.PW_ERR_NULL
+    assert a(ctypes.byref(shp), FAKE, FAKE, FAKE, 17, FAKE, ws, need, None) == pw.PW_ERR_UNSUPPORTED
+    assert a(ctypes.byref(shp), FAKE, FAKE, FAKE, 8, FAKE, ws, need - 1, None) == pw.PW_ERR_WORKSPACE
+    # a tiled copy beyond the 2^31-byte reach of the kernels' 32-bit page offsets
+    big = _shape(T=4096 * 16, N_pages=4096, H_q=64, H_kv=64, D=128)
+    assert t(ctypes.byref(big), FAKE, FAKE, FAKE, ws, 1 << 40, None) == pw.PW_ERR_UNSUPPORTED
+    assert b"2 GiB" in pw._lib.pw_last_error()
+
+
 def test_head_range_validation():
     f = pw._lib.pw_union_attention_heads
     shp = _shape(H_kv=2, H_q=8)
@@ -98,6 +122,13 @@ def test_dense_union_validation():
     f = pw._lib.pw_dense_union_ref
     assert f(ctypes.byref(shp), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == pw.PW_ERR_NULL
     assert f(ctypes.byref(_shape(D=80)), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == pw.PW_ERR_UNSUPPORTED
+    # the pair-mode kernel reads the same re-tiled copy: rejected beyond 2^31 bytes
+    big = _shape(T=4096 * 16, N_pages=4096, H_q=64, H_kv=64, D=128)
+    assert f(ctypes.byref(big), *[FAKE] * 7, 1 << 40, None) == pw.PW_ERR_UNSUPPORTED
+    assert b"2 GiB" in pw._lib.pw_last_error()
+    big2 = _shape(T=2048 * 16, N_pages=2048, H_q=128, H_kv=128, D=128)
+    assert pw._lib.pw_dense_union_paired(ctypes.byref(big2), *[FAKE] * 8, 1 << 40, None) == pw.PW_ERR_UNSUPPORTED
+    assert b"2 GiB" in pw._lib.pw_last_error()
     need = pw._lib.pw_dense_union_ref_workspace_bytes(ctypes.byref(shp))
     if need > 0:
         assert f(ctypes.byref(shp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == pw.PW_ERR_WORKSPACE

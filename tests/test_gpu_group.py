@@ -39,8 +39,8 @@ def test_group_ids_bit_exact(name):
     assert np.array_equal(got, ref), f"{(got != ref).sum()} IDs differ"
 
 
-@pytest.mark.parametrize("W,g", [(32, 1), (32, 3), (64, 8), (96, 8), (128, 4), (256, 8), (200, 5), (256, 2),
-                                 (64, 16), (256, 16), (40, 16)])
+@pytest.mark.parametrize("W,g", [(32, 1), (33, 3), (64, 8), (96, 8), (128, 4), (256, 8), (200, 5), (256, 2),
+                                 (64, 16), (256, 16), (80, 10), (96, 12)])
 def test_group_windows_and_sizes(W, g):
     # random supports over N = 256 pages, including ragged last windows and groups
     log(f"[case] pw_group random W={W} g={g}")
@@ -54,7 +54,7 @@ def test_group_windows_and_sizes(W, g):
     assert np.array_equal(got, ref)
 
 
-@pytest.mark.parametrize("W,g", [(384, 8), (512, 8), (768, 4), (1024, 8), (1000, 16), (300, 5),
+@pytest.mark.parametrize("W,g", [(384, 8), (512, 8), (768, 4), (1024, 8), (960, 12), (300, 5),
                                  (1024, 1), (640, 16)])
 def test_group_wide_windows(W, g):
     # several waves share one window (W > 256); T = 2048 gives full and ragged windows

@@ -154,7 +154,9 @@ def test_invalid_arguments_raise():
 
 def test_largest_page_count():
     # N_pages = 32768 (the supported maximum) at P = 16: T = 524288 queries, identity groups;
-    # page offsets reach the top of the 32-bit range of the tiled copy
+    # the largest union list and page bitset; page offsets of the tiled copy reach
+    # 32768 * 64 * 64 = 2^27 bytes (the 2^31 limit of the offsets is checked on the host,
+    # test_abi.py)
     T, P, Hq, Hkv, D, S, g = 524288, 16, 4, 1, 64, 4, 8
     N = T // P
     log(f"[case] union largest N={N} T={T}")
@@ -170,7 +172,7 @@ def test_largest_page_count():
                        .view(torch.int16).numpy().view(np.uint16),
         "k_codes": torch.randn((N, Hkv, P, D), generator=gen).to(torch.float8_e4m3fn)
                         .view(torch.uint8).numpy(),
-        "v_codes": torch.randn((N, Hkv, D, P), generator=gen).to(torch.float8_e4m3fn)
+        "v_codes": torch.randn((N, Hkv, P, D), generator=gen).to(torch.float8_e4m3fn)
                         .view(torch.uint8).numpy(),
         "scales": rng.uniform(0.05, 1.0, size=(2, N, Hkv)).astype(np.float32),
         "sel_pages": sel,

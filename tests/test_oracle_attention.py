@@ -24,7 +24,7 @@ def test_all_pages_selected_is_full_causal_attention():
     qb, kc, vc, sc = inp["q_bits"], inp["k_codes"], inp["v_codes"], inp["scales"]
     q = torch.from_numpy(qb.view(np.int16)).view(torch.bfloat16).double()
     k = torch.from_numpy(kc).view(torch.float8_e4m3fn).double() * torch.from_numpy(sc[0]).double()[:, :, None, None]
-    v = torch.from_numpy(vc).view(torch.float8_e4m3fn).double().transpose(2, 3) * torch.from_numpy(sc[1]).double()[:, :, None, None]
+    v = torch.from_numpy(vc).view(torch.float8_e4m3fn).double() * torch.from_numpy(sc[1]).double()[:, :, None, None]
     k = k.permute(1, 0, 2, 3).reshape(Hkv, T, -1).repeat_interleave(2, dim=0)
     v = v.permute(1, 0, 2, 3).reshape(Hkv, T, -1).repeat_interleave(2, dim=0)
     ref = torch.nn.functional.scaled_dot_product_attention(q.transpose(0, 1), k, v, is_causal=True)

@@ -61,7 +61,7 @@ def test_kv_quantisation():
     wl = synth.WORKLOADS["tiny_1k"]
     d = synth.make_qkv(wl)
     kc, vc, sc = d["k_codes"], d["v_codes"], d["scales"]
-    assert kc.shape == (wl.N, wl.H_kv, wl.P, wl.D) and vc.shape == (wl.N, wl.H_kv, wl.D, wl.P)
+    assert kc.shape == (wl.N, wl.H_kv, wl.P, wl.D) and vc.shape == (wl.N, wl.H_kv, wl.P, wl.D)
     for codes in (kc, vc):
         vals = decode_e4m3fn(codes)
         assert not np.isnan(vals).any()
