@@ -61,8 +61,9 @@ pw_status check_tiled_workspace(const pw_shape* s, const void* ws, size_t ws_byt
   if (!ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
   if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
   if (((uintptr_t)ws & 255) != 0) return fail(PW_ERR_DIMS, "workspace must be 256-byte aligned");
-  if (need / 2 > 0x7FFFFFFFu)
-    return fail(PW_ERR_UNSUPPORTED, "tiled K/V of %zu bytes exceeds 2 GiB", need / 2);
+  if (pw::tiled_kv_bytes(*s) / 2 > 0x7FFFFFFFu)
+    return fail(PW_ERR_UNSUPPORTED, "tiled K/V of %zu bytes exceeds 2 GiB",
+                pw::tiled_kv_bytes(*s) / 2);
   return PW_OK;
 }
 

@@ -38,7 +38,7 @@
 // running max untouched on that page (alpha = 1 exactly), so its result is
 // the same whichever group it sits in; each (query, Q head) row is written
 // once, by its wave.  There are no atomics and no partial outputs.
-#include "pw_internal.h"
+#include "attn_common.h"
 
 #ifndef PW_UA_WG_WAVES
 #define PW_UA_WG_WAVES 4  // waves (independent groups) per workgroup
@@ -46,17 +46,6 @@
 
 namespace pw {
 namespace {
-
-constexpr float kLog2e = 1.4426950408889634f;
-// Lazy-rescale threshold (log2 units): a row's reference maximum moves only
-// when a score exceeds it by more than kTau, so p <= 2^kTau.  At 24, the
-// Cauchy-Schwarz bound below usually proves on N(0,1)-like data that no score
-// of a page can move the reference, and the wave skips its max pass.
-constexpr float kTau = 24.0f;
-// Relative slack of the norm bounds: covers the fp32 rounding of the sums of
-// squares, of the square roots and of the score accumulation, and the residual
-// of the two-part e4m3 split of Q (below 1e-4 of a row's norm).
-constexpr float kNormSlack = 1.0f + 1.0f / 512;
 
 struct UAParams {
   const uint16_t* Q;
@@ -87,42 +76,6 @@ struct UAParams {
 };
 
 enum : int { kUnionMode = 0, kPairMode = 1 };
-
-// Physical key held by MFMA row i of key tile kt.  Output register r of a lane
-// in half `hf` holds MFMA row 8*(r/4) + 4*hf + r%4; with this map it holds
-// key 32*hf + 16*kt + r, i.e. each lane sees 32 consecutive keys.
-__device__ __forceinline__ int tile_key(int i, int kt) {
-  return 32 * ((i >> 2) & 1) + 16 * kt + 4 * (i >> 3) + (i & 3);
-}
-
-// Maxima of scores that come straight from the matrix cores (never a
-// signalling NaN): plain v_max3 / v_max, without the quieting v_max x, x that
-// fmaxf adds per operand in IEEE mode.
-__device__ __forceinline__ float max3_raw(float a, float b, float c) {
-  float r;
-  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-  return r;
-}
-__device__ __forceinline__ float max_raw(float a, float b) {
-  float r;
-  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
-  return r;
-}
-
-// Lanes l and l ^ 32 hold the two key halves of the same query row: combine
-// them with one VALU lane swap (no LDS round trip).
-__device__ __forceinline__ float half_max(float x) {
-  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return max_raw(__uint_as_float(pr[0]), __uint_as_float(pr[1]));
-}
-__device__ __forceinline__ float half_sum(float x) {
-  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
-}
-
-__device__ __forceinline__ uint4 load16(const uint8_t* p) {
-  return *reinterpret_cast<const uint4*>(p);
-}
 
 // Re-tiles the FP8 pages of one layer into MFMA operand order (one workgroup
 // per (page, KV head) block of 64 key slots x D bytes, for K and for V; both
@@ -230,7 +183,6 @@ __global__ __launch_bounds__(256) void tile_kv_kernel(const uint8_t* __restrict_
 // pages they selected, unnormalised partials out (direct KV-page union).
 template <int D, int P, int MODE>
 __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAParams p) {
-  constexpr int NT = 1;          // one 32-row tile per wave
   // P in {16, 32, 64} keys per page; the tiled pages always hold 64 key slots
   // (slots >= P are zero and masked here).
   constexpr int KCH = D / 32;    // uint4 chunks of K per lane per key tile
@@ -368,87 +320,29 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   const int tmin = __builtin_amdgcn_readfirstlane(
       (int)wave_min_u32(my_t >= 0 ? (uint32_t)my_t : 0xFFFFFFFFu));
 
-  // ---- per-lane query rows and Q operands (B of S^T = K Q^T).  Each bf16 row
-  // is scaled by a power of two (absmax into [128, 256)) and split into two
-  // e4m3fn parts, hi + lo (exact for elements >= 2^-2 after scaling, within
-  // 2^-10 below), so that K^T can run on the FP8 MFMA straight from the cache
-  // bytes; 2^-e is folded back into the score scale.
-  constexpr int KQ = D / 64;     // fp8 MFMA k-steps (64 d each, 32 per lane half)
-  int slot[NT], trow[NT], qhead[NT], pslot[NT];
-  float rscale[NT], qn[NT];      // qn: bound on the norm of the row's hi + lo (scaled)
-  i32x8 qhi[NT][KQ], qlo[NT][KQ];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int n = 32 * (rt + nt) + col;
-    const int s = n / p.G;
-    const int t = __shfl(my_t, s & 63);
-    const bool ok = (s < gm) && (t >= 0);
-    slot[nt] = ok ? s : -1;
-    trow[nt] = ok ? t : -1;
-    pslot[nt] = __shfl(my_slot, s & 63);
-    qhead[nt] = h * p.G + (n - s * p.G);
-    const uint16_t* qp = p.Q + ((size_t)(ok ? t : 0) * p.Hq + qhead[nt]) * D + (D / 2) * hf;
-    float q[D / 2];
-#pragma unroll
-    for (int c = 0; c < D / 16; ++c) {
-      const uint4 v = ok ? *reinterpret_cast<const uint4*>(qp + 8 * c) : make_uint4(0, 0, 0, 0);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        q[8 * c + 2 * k] = __uint_as_float(w[k] << 16);
-        q[8 * c + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-      }
-    }
-    float amax = 0.f;
-#pragma unroll
-    for (int i = 0; i < D / 2; ++i) amax = fmaxf(amax, fabsf(q[i]));
-    amax = fmaxf(amax, __shfl_xor(amax, 32));
-    int e = 0;
-    if (amax > 0.f) {
-      int ex;
-      frexpf(amax, &ex);
-      e = 8 - ex;                  // amax * 2^e in [128, 256)
-    }
-    rscale[nt] = ldexpf(1.f, -e);
-    float ssq = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < KQ; ++ks) {
-#pragma unroll
-      for (int w = 0; w < 8; ++w) {
-        const float* x = q + 32 * ks + 4 * w;
-        const float x0 = ldexpf(x[0], e), x1 = ldexpf(x[1], e);
-        const float x2 = ldexpf(x[2], e), x3 = ldexpf(x[3], e);
-        ssq = fmaf(x0, x0, fmaf(x1, x1, fmaf(x2, x2, fmaf(x3, x3, ssq))));
-        int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
-        hi = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hi, true);
-        const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-        const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01[0], x1 - h01[1], 0, false);
-        lo = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23[0], x3 - h23[1], lo, true);
-        qhi[nt][ks][w] = hi;
-        qlo[nt][ks][w] = lo;
-      }
-    }
-    qn[nt] = sqrtf(ssq + __shfl_xor(ssq, 32)) * kNormSlack;
-  }
+  // ---- the lane's query row (32 rows per wave: row n = slot * G + head)
+  const int n = 32 * rt + col;
+  const int s_ = n / p.G;
+  const int t_ = __shfl(my_t, s_ & 63);
+  const bool ok = (s_ < gm) && (t_ >= 0);
+  const int slot = ok ? s_ : -1, trow = ok ? t_ : -1;
+  const int pslot = __shfl(my_slot, s_ & 63);
+  const int qhead = h * p.G + (n - s_ * p.G);
+  QRow<D> qr;
+  load_q_row<D>(p.Q + ((size_t)(ok ? t_ : 0) * p.Hq + qhead) * D + (D / 2) * hf, ok, qr);
 
-  float m_run[NT], l_run[NT];
-  f32x16 acc[NT][DT];
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x16 acc[DT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    m_run[nt] = -INFINITY;
-    l_run[nt] = 0.f;
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[nt][dt][r] = 0.f;
-  }
+    for (int r = 0; r < 16; ++r) acc[dt][r] = 0.f;
 
   // K and V come from the tiled copies (tile_kv_kernel): the block of (page u,
   // KV head h) holds 64 key slots x D in MFMA operand order, so every load
   // below is one contiguous 1 KB read of the wave (lane l at 16 * l).
   uint4 kbuf[2][KCH], vbuf[DT][2];
-  f32x16 sacc[NT][2];
+  f32x16 sacc[2];
   float4 pfr = make_float4(0.f, 0.f, 0.f, 0.f);
   auto page_of = [&](int i) {       // wave-uniform
     return __builtin_amdgcn_readfirstlane((int)(list[min(i, n_u - 1)] & 0xFFFF));
@@ -481,128 +375,6 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
                                                   vrs, loff, so + 1024 * (2 * dt + j), 0));
   };
   const float4* pfac = p.pf + h;                            // [N][Hkv]
-  // S^T = K (Qhi + Qlo)^T on the FP8 MFMA
-  auto qk = [&](const uint4 (&kr)[2][KCH], f32x16 (&sc)[NT][2]) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sc[nt][kt][r] = 0.f;
-    // key tiles innermost: consecutive MFMAs accumulate into different tiles
-#pragma unroll
-    for (int ks = 0; ks < KQ; ++ks) {
-#pragma unroll
-      for (int part = 0; part < 2; ++part) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-          const uint4 w0 = kr[kt][2 * ks], w1 = kr[kt][2 * ks + 1];
-          const i32x8 a = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w,
-                           (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt)
-            sc[nt][kt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                a, part ? qlo[nt][ks] : qhi[nt][ks], sc[nt][kt], 0, 0, 0, 127, 0, 127);
-        }
-      }
-    }
-  };
-  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-  // ---- stages of one page: mask -> softmax -> (rescale) -> PV
-  // causal / page-size mask, only where some key can lie after a member
-  auto mask_page = [&](f32x16 (&sc)[NT][2], int u) {
-    const bool need_mask = P < 64 || (u * P + P - 1 > tmin);
-    if (need_mask) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = 32 * hf + 16 * kt + r;
-            if (key >= P || u * P + key > trow[nt]) sc[nt][kt][r] = -INFINITY;
-          }
-    }
-  };
-  // online softmax in the log2 domain, v_scale folded into the exponent; the
-  // probabilities are produced as bf16 MFMA operands; returns the rescale
-  // factor of the accumulator (1 unless the reference max moved)
-  auto softmax = [&](f32x16 (&sc)[NT][2], uint32_t mbits, const float4 f,
-                     bf16x8 (&pB)[NT][4], float (&alph)[NT]) {
-    const float ksc0 = f.x, kb0 = f.y;
-    const float lvs = f.z;    // log2(v_scale)
-    const float ivs = f.w;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const bool member = slot[nt] >= 0 && ((mbits >> slot[nt]) & 1u);
-      const float ksc = ksc0 * rscale[nt];
-      const float lim = m_run[nt] + kTau;
-      // Cauchy-Schwarz: no score of the row on this page exceeds
-      // |q| * max |k| * |scale|; when that cannot pass the reference by kTau
-      // for any member row, the row maxima are not needed (the computed
-      // maximum would leave every reference where it is: same result).
-      const bool may_move = member && !(qn[nt] * kb0 * rscale[nt] <= lim);
-      float m_new = m_run[nt], alpha = 1.f;
-      if (__ballot(may_move)) {
-        float mx = max_raw(sc[nt][0][0], sc[nt][0][1]);
-#pragma unroll
-        for (int i = 2; i < 32; i += 2)
-          mx = max3_raw(mx, sc[nt][i >> 4][i & 15], sc[nt][i >> 4][(i & 15) + 1]);
-        mx = half_max(mx);
-        const float mx2 = mx * ksc;
-        m_new = (member && mx2 > lim) ? mx2 : m_run[nt];
-        // exp2(0) = 1 exactly when the reference max is unchanged
-        alpha = __builtin_amdgcn_exp2f((m_new == m_run[nt]) ? 0.f : m_run[nt] - m_new);
-      }
-      m_run[nt] = m_new;
-      const float bias = (member && m_new > -INFINITY) ? (lvs - m_new) : -INFINITY;
-      float ps = 0.f;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        bf16x8 v;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float e0 = __builtin_amdgcn_exp2f(fmaf(sc[nt][q >> 1][8 * (q & 1) + e], ksc, bias));
-          const float e1 = __builtin_amdgcn_exp2f(fmaf(sc[nt][q >> 1][8 * (q & 1) + e + 1], ksc, bias));
-          bf16x2 pr;
-          pr[0] = (__bf16)e0;
-          pr[1] = (__bf16)e1;
-          ps = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, ps, false);
-          v[e] = pr[0];
-          v[e + 1] = pr[1];
-        }
-        pB[nt][q] = v;
-      }
-      l_run[nt] = l_run[nt] * alpha + ps * ivs;
-      alph[nt] = alpha;
-    }
-  };
-  auto rescale = [&](const float (&alph)[NT]) {
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      if (__ballot(alph[nt] != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[nt][dt][r] *= alph[nt];
-      }
-    }
-  };
-  // O^T += V^T P^T  (d tiles innermost: consecutive MFMAs are independent)
-  auto pv = [&](const uint4 (&vr)[DT][2], const bf16x8 (&pB)[NT][4]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        const uint4 w = vr[dt][q >> 1];
-        const bf16x8 a = (q & 1) ? fp8x8_to_bf16(w.z, w.w) : fp8x8_to_bf16(w.x, w.y);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          acc[nt][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pB[nt][q], acc[nt][dt], 0, 0, 0);
-      }
-    }
-  };
 
   // One page of K/V ahead, two waves per SIMD overlapping each other's matrix
   // and vector work.  (Software-pipelined schedules that keep the next page's
@@ -614,60 +386,39 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
     load_v(vbuf, u0);
     pfr = pfac[(size_t)u0 * p.Hkv];
   }
-  bf16x8 pB[NT][4];
-  float alph[NT];
+  bf16x8 pB[4];
   for (int up = 0; up < n_u; ++up) {
     const uint32_t ent = __builtin_amdgcn_readfirstlane(list[up]);
     const float4 pf_c = pfr;
     const int u1 = page_of(up + 1);
-    qk(kbuf, sacc);
+    qk_page<D>(kbuf, qr, sacc);
     load_k(kbuf, u1);                     // K registers are free once the MFMAs have read them
     pfr = pfac[(size_t)u1 * p.Hkv];
-    mask_page(sacc, ent & 0xFFFF);
-    softmax(sacc, ent >> 16, pf_c, pB, alph);
-    rescale(alph);
-    pv(vbuf, pB);
+    mask_page<P>(sacc, ent & 0xFFFF, tmin, trow, hf);
+    const bool member = slot >= 0 && (((ent >> 16) >> slot) & 1u);
+    const float alpha = softmax_page(sacc, member, pf_c, qr.rscale, qr.qn, m_run, l_run, pB);
+    rescale_acc<D>(acc, alpha);
+    pv_page<D>(vbuf, pB, acc);
     load_v(vbuf, u1);
   }
 
   if constexpr (MODE == kPairMode) {
     // ---- partials of the page pair: (m, l, acc) per owned row, merged later
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const float l_tot = half_sum(l_run[nt]);
-      if (trow[nt] < 0) continue;
-      float* pp = p.partials + ((size_t)pslot[nt] * p.G + (qhead[nt] - h * p.G)) * (D + 4);
-      if (hf == 0) *reinterpret_cast<float2*>(pp) = make_float2(m_run[nt], l_tot);
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq)
-          *reinterpret_cast<float4*>(pp + 4 + 32 * dt + 8 * rq + 4 * hf) =
-              make_float4(acc[nt][dt][4 * rq], acc[nt][dt][4 * rq + 1], acc[nt][dt][4 * rq + 2],
-                          acc[nt][dt][4 * rq + 3]);
-    }
-    return;
-  }
-  // ---- epilogue: normalise and write each owned row once
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const float l_tot = half_sum(l_run[nt]);
-    const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
-    if (trow[nt] < 0) continue;
-    uint16_t* op = p.O + ((size_t)trow[nt] * p.Hq + qhead[nt]) * D;
+    const float l_tot = half_sum(l_run);
+    if (trow < 0) return;
+    float* pp = p.partials + ((size_t)pslot * p.G + (qhead - h * p.G)) * (D + 4);
+    if (hf == 0) *reinterpret_cast<float2*>(pp) = make_float2(m_run, l_tot);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        bf16x2 lo, hi;
-        lo[0] = (__bf16)(acc[nt][dt][4 * rq + 0] * inv);
-        lo[1] = (__bf16)(acc[nt][dt][4 * rq + 1] * inv);
-        hi[0] = (__bf16)(acc[nt][dt][4 * rq + 2] * inv);
-        hi[1] = (__bf16)(acc[nt][dt][4 * rq + 3] * inv);
-        uint2 v = make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
-        *reinterpret_cast<uint2*>(op + 32 * dt + 8 * rq + 4 * hf) = v;
-      }
+      for (int rq = 0; rq < 4; ++rq)
+        *reinterpret_cast<float4*>(pp + 4 + 32 * dt + 8 * rq + 4 * hf) =
+            make_float4(acc[dt][4 * rq], acc[dt][4 * rq + 1], acc[dt][4 * rq + 2],
+                        acc[dt][4 * rq + 3]);
+    return;
   }
+  // ---- epilogue: normalise and write each owned row once
+  store_row<D>(acc, l_run, trow >= 0 ? p.O + ((size_t)trow * p.Hq + qhead) * D : nullptr, hf);
 }
 
 
