@@ -96,8 +96,8 @@ def pair_entries(sel: np.ndarray, pairs, N: int) -> float:
     return tot / (H * T)
 
 
-KERNEL_FILES = ("query_union_paged_amd/csrc/union_attn.hip", "query_union_paged_amd/csrc/pw_internal.h",
-                "query_union_paged_amd/build.py")
+KERNEL_FILES = ("query_union_paged_amd/csrc/union_attn.hip", "query_union_paged_amd/csrc/attn_common.h",
+                "query_union_paged_amd/csrc/pw_internal.h", "query_union_paged_amd/build.py")
 
 
 def kernel_hash() -> str:
