@@ -194,6 +194,32 @@ pw_status pw_union_attention(const pw_shape* shape, const uint16_t* Q,
                              void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * pw_union_attention_noalloc -- pw_union_attention without a workspace.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, result and errors as pw_union_attention minus the workspace: the
+ * re-tiled K/V copy and page factors live in a device array inside the
+ * library, PW_NOALLOC_SCRATCH_BYTES (160 MiB) on each device the library runs
+ * on, held until the process ends.  The call allocates nothing; its first call
+ * on a device looks up that device's array (hipGetSymbolAddress).
+ *
+ * Limit: pw_union_attention_workspace_bytes(shape) <= PW_NOALLOC_SCRATCH_BYTES
+ * (e.g. 1024 pages x 8 KV heads at D = 128 need 134 MB), else
+ * PW_ERR_UNSUPPORTED.  Every call on a device uses that device's one array,
+ * which keeps the last call's contents: calls that overlap on one device
+ * (concurrent streams or threads) race and give unspecified results; calls on
+ * one stream are ordered and safe.  Nothing needs clearing between calls (each
+ * call rewrites all it reads).
+ * ------------------------------------------------------------------------- */
+#define PW_NOALLOC_SCRATCH_BYTES ((size_t)160 << 20)
+pw_status pw_union_attention_noalloc(const pw_shape* shape, const uint16_t* Q,
+                                     const uint8_t* K_fp8, const uint8_t* V_fp8,
+                                     const float* scales, const int32_t* sel_pages,
+                                     const int32_t* query_ids, int32_t g, uint16_t* O,
+                                     void* stream);
+
+/* ---------------------------------------------------------------------------
  * pw_tile_kv / pw_union_attention_tiled -- the two halves of
  * pw_union_attention.
  *

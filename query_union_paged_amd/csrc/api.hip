@@ -171,6 +171,34 @@ pw_status pw_union_attention_heads(const pw_shape* shape, const uint16_t* Q,
                                h_count, O, ws, ws_bytes, stream, "pw_union_attention_heads launch");
 }
 
+pw_status pw_union_attention_noalloc(const pw_shape* shape, const uint16_t* Q,
+                                     const uint8_t* K_fp8, const uint8_t* V_fp8,
+                                     const float* scales, const int32_t* sel_pages,
+                                     const int32_t* query_ids, int32_t g, uint16_t* O,
+                                     void* stream) {
+  pw_status st = check_shape(shape);
+  if (st != PW_OK) return st;
+  if (!Q || !K_fp8 || !V_fp8 || !scales || !sel_pages || !query_ids || !O)
+    return fail(PW_ERR_NULL, "Q, K_fp8, V_fp8, scales, sel_pages, query_ids and O are required");
+  st = check_attention_support(shape, g);
+  if (st != PW_OK) return st;
+  const size_t need = pw::tiled_kv_bytes(*shape);
+  if (need > PW_NOALLOC_SCRATCH_BYTES)
+    return fail(PW_ERR_UNSUPPORTED,
+                "re-tiled K/V of %zu bytes exceeds the %zu-byte no-alloc scratch "
+                "(use pw_union_attention with a workspace)",
+                need, (size_t)PW_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  hipError_t e = pw::noalloc_scratch(&ws, &ws_bytes);
+  if (e != hipSuccess) return hip_status(e, "pw_union_attention_noalloc scratch lookup");
+  if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "no-alloc scratch %zu < %zu bytes", ws_bytes, need);
+  return hip_status(pw::launch_union_attention(*shape, Q, K_fp8, V_fp8, scales, sel_pages,
+                                               query_ids, g, 0, shape->H_kv, O, ws,
+                                               (hipStream_t)stream),
+                    "pw_union_attention_noalloc launch");
+}
+
 pw_status pw_tile_kv(const pw_shape* shape, const uint8_t* K_fp8, const uint8_t* V_fp8,
                      const float* scales, void* ws, size_t ws_bytes, void* stream) {
   pw_status st = check_shape(shape);

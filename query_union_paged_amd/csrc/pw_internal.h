@@ -60,6 +60,9 @@ hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uin
                                  const float* scales, const int2* plist, const int* pcount,
                                  const int* tstart, const int2* pairs, int tiles_head,
                                  float* partials, int Np, int Tc, int t0, hipStream_t stream);
+// Device address and size of the calling device's no-alloc scratch array
+// (looked up once per device).
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
 size_t check_ids_workspace(const pw_shape& s);
 hipError_t launch_check_ids(const pw_shape& s, const int32_t* ids, int32_t* bad, void* ws,
                             hipStream_t stream);

@@ -50,6 +50,7 @@ _SIGS = {
     "pw_union_attention": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "pw_union_attention_heads": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp,
                                         _vp, _sz, _vp]),
+    "pw_union_attention_noalloc": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp]),
     "pw_tile_kv": (_i32, [_SHP, _vp, _vp, _vp, _vp, _sz, _vp]),
     "pw_union_attention_tiled": (_i32, [_SHP, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "pw_check_ids_workspace_bytes": (_sz, [_SHP]),
@@ -154,6 +155,29 @@ def pw_union_attention(shp: PWShape, Q, K_fp8, V_fp8, scales, sel_pages, query_i
                                              int(heads[0]), int(heads[1]), o, ws,
                                              workspace.numel(), _stream(stream)),
                "pw_union_attention_heads")
+    return O
+
+
+NOALLOC_SCRATCH_BYTES = 160 << 20
+
+
+def pw_union_attention_noalloc(shp: PWShape, Q, K_fp8, V_fp8, scales, sel_pages, query_ids,
+                               g: int, O: Optional[torch.Tensor] = None,
+                               stream=None) -> torch.Tensor:
+    """pw_union_attention with the library's own device scratch instead of a workspace (for
+    callers that cannot allocate: calls on one device share that scratch)."""
+    T, Hq, Hkv, D, P, N, S = shp.T, shp.H_q, shp.H_kv, shp.D, shp.P, shp.N_pages, shp.S
+    q = _dev(Q, "Q", _BF16, (T, Hq, D))
+    k = _dev(K_fp8, "K_fp8", _U8, (N, Hkv, P, D))
+    v = _dev(V_fp8, "V_fp8", _U8, (N, Hkv, P, D))
+    sc = _dev(scales, "scales", (torch.float32,), (2, N, Hkv))
+    sel = _dev(sel_pages, "sel_pages", (torch.int32,), (Hkv, T, S))
+    ids = _dev(query_ids, "query_ids", (torch.int32,), (Hkv, T))
+    if O is None:
+        O = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=Q.device)
+    o = _dev(O, "O", _BF16, (T, Hq, D))
+    _check(_lib.pw_union_attention_noalloc(ctypes.byref(shp), q, k, v, sc, sel, ids, g, o,
+                                           _stream(stream)), "pw_union_attention_noalloc")
     return O
 
 

@@ -106,6 +106,22 @@ def test_tiled_validation():
     assert b"2 GiB" in pw._lib.pw_last_error()
 
 
+def test_noalloc_validation():
+    # host-side checks of the no-alloc entry point, before any HIP call: required pointers,
+    # the support set, and shapes whose re-tiled K/V exceeds the fixed scratch
+    f = pw._lib.pw_union_attention_noalloc
+    shp = _shape()
+    assert f(ctypes.byref(shp), None, *[FAKE] * 5, 8, FAKE, None) == pw.PW_ERR_NULL
+    assert f(ctypes.byref(shp), *[FAKE] * 6, 8, None, None) == pw.PW_ERR_NULL
+    assert f(ctypes.byref(shp), *[FAKE] * 6, 17, FAKE, None) == pw.PW_ERR_UNSUPPORTED
+    big = _shape(T=2048 * 64, N_pages=2048, P=64, H_q=32, H_kv=8, D=128)   # 268 MB re-tiled
+    assert pw._lib.pw_union_attention_workspace_bytes(ctypes.byref(big), 8) > pw.NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), *[FAKE] * 6, 8, FAKE, None) == pw.PW_ERR_UNSUPPORTED
+    assert b"no-alloc scratch" in pw._lib.pw_last_error()
+    fits = _shape(T=1024 * 64, N_pages=1024, P=64, H_q=32, H_kv=8, D=128)  # the 64K layer: 134 MB
+    assert pw._lib.pw_union_attention_workspace_bytes(ctypes.byref(fits), 8) <= pw.NOALLOC_SCRATCH_BYTES
+
+
 def test_head_range_validation():
     f = pw._lib.pw_union_attention_heads
     shp = _shape(H_kv=2, H_q=8)
