@@ -14,6 +14,9 @@ from oracle.attention import Problem, attention_pairs_parallel
 # compared elements (derivation in the design notes).
 TOL_MAX = 2e-2
 TOL_MEAN = 2e-3
+# relative RMS error ||dO|| / ||O|| over the compared rows: the bf16 rounding of the
+# output alone gives about 2^-9 / sqrt(3) ~ 1.1e-3; gated at 5e-3
+TOL_REL_RMS = 5e-3
 
 WORKERS = max(1, min(16, len(os.sched_getaffinity(0))))
 
@@ -49,6 +52,21 @@ def sample_pairs(wl, n_windows=2, n_random=96, seed=0):
     return sorted(set(pairs))
 
 
+def window_sample_pairs(wl, every=16, seed=0, n_random=96):
+    """(h, t) pairs of every `every`-th window of every head plus its first two and last two
+    windows, and `n_random` random queries per head (large-workload parity sample)."""
+    rng = np.random.default_rng(seed)
+    T, W = wl.T, wl.W
+    n_win = -(-T // W)
+    wins = sorted(set(range(0, n_win, every)) | {0, 1, n_win - 2, n_win - 1} - {-1})
+    pairs = []
+    for h in range(wl.H_kv):
+        for w in wins:
+            pairs += [(h, t) for t in range(w * W, min(T, (w + 1) * W))]
+        pairs += [(h, int(t)) for t in rng.choice(T, size=min(n_random, T), replace=False)]
+    return sorted(set(pairs))
+
+
 def oracle_rows(inp: dict, pairs):
     t0 = time.time()
     ref = attention_pairs_parallel(problem(inp), pairs, workers=WORKERS)
@@ -74,5 +92,6 @@ def assert_close(got, ref, what=""):
     assert np.isfinite(got).all(), f"{what}: non-finite output"
     e = errors(got, ref)
     log(f"[parity] {what}: max {e['max']:.3e} mean {e['mean']:.3e} rel_rms {e['rel_rms']:.3e}")
-    assert e["max"] <= TOL_MAX and e["mean"] <= TOL_MEAN, f"{what}: {e}"
+    assert e["max"] <= TOL_MAX and e["mean"] <= TOL_MEAN and e["rel_rms"] <= TOL_REL_RMS, \
+        f"{what}: {e}"
     return e

@@ -5,7 +5,7 @@ import torch
 
 from query_union_paged_amd import synth
 from tests.gpu_common import (assert_close, gpu_rows, host_inputs, log, oracle_rows,
-                              sample_pairs)
+                              sample_pairs, window_sample_pairs)
 from tests.oracle_helpers import tiny_problem
 
 pytestmark = pytest.mark.gpu
@@ -122,9 +122,10 @@ def test_edge_cases_in_selection():
                                        ("prefill_64k", ["regroup", "identity", "g1"]),
                                        ("prefill_64k_70b", ["regroup", "identity"])])
 def test_large_sampled(name, arms):
+    # every 16th window of every head, the first and last two windows, 96 random queries per head
     wl = synth.WORKLOADS[name]
     inp = host_inputs(name)
-    pairs = sample_pairs(wl)
+    pairs = window_sample_pairs(wl)
     ref = oracle_rows(inp, pairs)
     log(f"[case] union {name}: {len(pairs)} sampled rows")
     for arm in arms:
