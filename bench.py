@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_64k")
     ap.add_argument("--no-arms", action="store_true", help="skip the identity / g=1 comparison arms")
-    ap.add_argument("--only-arm", choices=["selector"], default=None,
+    ap.add_argument("--only-arm", choices=["selector", "dense"], default=None,
                     help="run only this comparison arm (for profiling it)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle sample time")
@@ -239,6 +239,33 @@ def head_pipeline_arm(pw, torch, wl, dev, shp, O, ws, reps: int = 10):
     return out
 
 
+def dense_arms(pw, torch, wl, inp, dev, shp, O, calls, cold_ms, F_u):
+    """The direct KV-page union (design-study comparison), with adjacent pairs and with affinity
+    pairs from the device's greedy co-selection matching (cold calls)."""
+    q, k, v, sc, sel = dev["q_bits"], dev["k_codes"], dev["v_codes"], dev["scales"], dev["sel_pages"]
+    arms = {}
+    dws = torch.empty(pw.pw_dense_union_ref_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
+    dense = lambda: pw.pw_dense_union_ref(shp, q, k, v, sc, sel, O=O, workspace=dws)
+    ms = cold_ms([dense], n=2)
+    arms["direct_page_union"] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12,
+                                 "workspace_GiB": dws.numel() / 2 ** 30,
+                                 "entries_per_query": pair_entries(inp["sel_pages"], None, wl.N)}
+    # the same with affinity pairs (greedy co-selection matching on the device)
+    pws = torch.empty(pw.pw_page_pairs_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
+    prs = pw.pw_page_pairs(shp, sel, workspace=pws)
+    pairing = lambda: pw.pw_page_pairs(shp, sel, pairs=prs, workspace=pws)
+    dense_p = lambda: pw.pw_dense_union_ref(shp, q, k, v, sc, sel, O=O, workspace=dws, pairs=prs)
+    calls.run([pairing, dense_p], 1, cold=False)
+    t = np.median(calls.run([pairing, dense_p], 2, cold=True), axis=0)
+    arms["direct_page_union_affinity"] = {
+        "pairing_ms": float(t[0]), "union_ms": float(t[1]), "ms": float(t.sum()),
+        "useful_TFLOPs": F_u / (float(t.sum()) * 1e-3) / 1e12,
+        "entries_per_query": pair_entries(inp["sel_pages"], prs.cpu().numpy(), wl.N)}
+    log(f"[bench] direct page union: adjacent {ms:.2f} ms, affinity {t[0]:.2f} + {t[1]:.2f} ms")
+    del dws, pws
+    return arms
+
+
 def selector_arm(pw, torch, wl, dev, shp, O, ws, ident, cold_ms):
     """The synthetic GPU selector (sink + 2 local pages + top pages by block key sums) and the
     complete call on its selections, regrouped and with identity grouping (cold calls)."""
@@ -395,6 +422,8 @@ def main():
     ident = torch.arange(wl.T, dtype=torch.int32, device="cuda").repeat(wl.H_kv, 1).contiguous()
     if args.only_arm == "selector":
         arms["selector"] = selector_arm(pw, torch, wl, dev, shp, O, ws, ident, cold_ms)
+    elif args.only_arm == "dense":
+        arms.update(dense_arms(pw, torch, wl, inp, dev, shp, O, calls, cold_ms, F_u))
     elif not args.no_arms:
         for name, g_arm in [("identity_union8", wl.g), ("per_query_g1", 1)]:
             ms = cold_ms([tile, attend(ident, g_arm)], n=5 if g_arm == 1 else 10)
@@ -402,26 +431,7 @@ def main():
             arms[name] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12,
                           "union_pages_mean": float(us.mean()), "union_pages_total": int(us.sum())}
         arms["regroup_gain_vs_identity"] = arms["identity_union8"]["ms"] / ms_per_step
-        # the direct KV-page union (design-study comparison)
-        dws = torch.empty(pw.pw_dense_union_ref_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
-        dense = lambda: pw.pw_dense_union_ref(shp, q, k, v, sc, sel, O=O, workspace=dws)
-        ms = cold_ms([dense], n=2)
-        arms["direct_page_union"] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12,
-                                     "workspace_GiB": dws.numel() / 2 ** 30,
-                                     "entries_per_query": pair_entries(inp["sel_pages"], None, wl.N)}
-        # the same with affinity pairs (greedy co-selection matching on the device)
-        pws = torch.empty(pw.pw_page_pairs_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
-        prs = pw.pw_page_pairs(shp, sel, workspace=pws)
-        pairing = lambda: pw.pw_page_pairs(shp, sel, pairs=prs, workspace=pws)
-        dense_p = lambda: pw.pw_dense_union_ref(shp, q, k, v, sc, sel, O=O, workspace=dws, pairs=prs)
-        calls.run([pairing, dense_p], 1, cold=False)
-        t = np.median(calls.run([pairing, dense_p], 2, cold=True), axis=0)
-        arms["direct_page_union_affinity"] = {
-            "pairing_ms": float(t[0]), "union_ms": float(t[1]), "ms": float(t.sum()),
-            "useful_TFLOPs": F_u / (float(t.sum()) * 1e-3) / 1e12,
-            "entries_per_query": pair_entries(inp["sel_pages"], prs.cpu().numpy(), wl.N)}
-        log(f"[bench] direct page union: adjacent {ms:.2f} ms, affinity {t[0]:.2f} + {t[1]:.2f} ms")
-        del dws, pws
+        arms.update(dense_arms(pw, torch, wl, inp, dev, shp, O, calls, cold_ms, F_u))
         arms["selector"] = selector_arm(pw, torch, wl, dev, shp, O, ws, ident, cold_ms)
         arms["head_pipeline"] = head_pipeline_arm(pw, torch, wl, dev, shp, O, ws)
 

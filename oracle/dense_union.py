@@ -66,8 +66,52 @@ def affinity_pairs(sel_h: np.ndarray, N: int) -> List[Pair]:
         a, b = int(u[i]), int(v[i])
         if mate[a] < 0 and mate[b] < 0:
             mate[a], mate[b] = b, a
+    return pairs_from_mates(mate)
+
+
+def pairs_from_mates(mate: np.ndarray) -> List[Pair]:
+    """Pair list (numbered by lower page) from a mate array (-1 = single)."""
+    N = mate.shape[0]
     return [(a, int(mate[a]) if mate[a] > a else -1) for a in range(N)
             if mate[a] < 0 or mate[a] > a]
+
+
+def matching_weight(co: np.ndarray, pairs: Sequence[Pair]) -> int:
+    """Sum of co[a][b] over the pairs (singles add 0): the (query, pair) entries the pairing
+    saves against one entry per selected page."""
+    return int(sum(co[a, b] for a, b in pairs if b >= 0))
+
+
+def max_coselection_pairs(sel_h: np.ndarray, N: int) -> List[Pair]:
+    """A maximum co-selection matching of one KV head's pages: pairs of distinct pages, each
+    page in at most one pair, maximising the sum of co[u][v] over the pairs (the reading of
+    "max co-selection matching"; unmatched pages stay single).
+
+    Written as the matching integer program, one 0/1 variable per edge with co > 0, one
+    "at most one edge per page" row per page, solved exactly (HiGHS branch and bound with
+    zero optimality gap).  Several matchings can reach the maximum: only the weight is unique.
+    """
+    from scipy.optimize import Bounds, LinearConstraint, milp
+    from scipy.sparse import csr_matrix
+    co = coselection(sel_h, N)
+    u, v = np.nonzero(np.triu(co, 1) > 0)
+    if u.size == 0:
+        return pairs_from_mates(np.full(N, -1, dtype=np.int64))
+    E = u.size
+    rows = np.concatenate([u, v])
+    cols = np.concatenate([np.arange(E), np.arange(E)])
+    A = csr_matrix((np.ones(2 * E), (rows, cols)), shape=(N, E))
+    res = milp(c=-co[u, v].astype(np.float64), constraints=LinearConstraint(A, 0, 1),
+               integrality=np.ones(E), bounds=Bounds(0, 1),
+               options={"mip_rel_gap": 0.0, "presolve": True})
+    if res.status != 0:
+        raise RuntimeError(f"matching program not solved: {res.message}")
+    x = np.rint(res.x).astype(np.int64)
+    assert np.all(np.abs(res.x - x) < 1e-6) and np.all(A @ x <= 1)
+    mate = np.full(N, -1, dtype=np.int64)
+    for e in np.nonzero(x)[0]:
+        mate[u[e]], mate[v[e]] = v[e], u[e]
+    return pairs_from_mates(mate)
 
 
 def pair_lists(pb: Problem, h: int, pairs: Optional[Sequence[Pair]] = None

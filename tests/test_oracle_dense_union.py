@@ -138,3 +138,83 @@ def test_affinity_partials_merge_to_the_per_query_result(seed):
     pairing = {h: affinity_pairs(inp["sel_pages"][h], pb.N) for h in range(pb.H_kv)}
     assert any(b >= 0 and b != a + 1 for pr in pairing.values() for a, b in pr)   # not adjacent
     np.testing.assert_allclose(dense_union(pb, pairing), attention(pb), rtol=0, atol=1e-12)
+
+
+# ---- the maximum co-selection matching (exact integer program) ----------------------------
+
+def _brute_max_weight(co, N):
+    """Best total weight over every matching of N pages, by exhaustive recursion."""
+    best = 0
+
+    def rec(free, w):
+        nonlocal best
+        best = max(best, w)
+        if len(free) < 2:
+            return
+        a = free[0]
+        rest = free[1:]
+        rec(rest, w)                                  # a stays single
+        for i, b in enumerate(rest):
+            if co[a][b] > 0:
+                rec(rest[:i] + rest[i + 1:], w + co[a][b])
+    rec(list(range(N)), 0)
+    return best
+
+
+def _is_matching(pairs, N):
+    seen = [p for pr in pairs for p in pr if p >= 0]
+    return sorted(seen) == list(range(N)) and all(b == -1 or a < b for a, b in pairs)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_max_matching_equals_exhaustive_search(seed):
+    from oracle.dense_union import matching_weight, max_coselection_pairs
+    rng = np.random.default_rng(100 + seed)
+    N = int(rng.integers(4, 10))
+    T = 40
+    sel_h = np.full((T, 4), -1, dtype=np.int32)
+    for t in range(T):
+        k = int(rng.integers(1, 5))
+        sel_h[t, :k] = rng.choice(N, size=k, replace=False)
+    # set-based counts, independent of coselection()
+    sup = [set(int(u) for u in row if 0 <= u < N) for row in sel_h]
+    co = [[sum(1 for s in sup if a in s and b in s) if a != b else 0 for b in range(N)]
+          for a in range(N)]
+    pairs = max_coselection_pairs(sel_h, N)
+    assert _is_matching(pairs, N)
+    assert matching_weight(np.array(co), pairs) == _brute_max_weight(co, N)
+
+
+def test_max_matching_beats_greedy_on_a_path():
+    # path 0-1-2-3 with co = 2, 3, 2: the greedy takes (1, 2) (weight 3), the maximum
+    # matching takes (0, 1) and (2, 3) (weight 4)
+    from oracle.dense_union import affinity_pairs, matching_weight, max_coselection_pairs
+    rows = [[0, 1]] * 2 + [[1, 2]] * 3 + [[2, 3]] * 2
+    sel_h = np.array([r + [-1] for r in rows], dtype=np.int32)
+    co = coselection(sel_h, 4)
+    assert affinity_pairs(sel_h, 4) == [(0, -1), (1, 2), (3, -1)]
+    assert max_coselection_pairs(sel_h, 4) == [(0, 1), (2, 3)]
+    assert matching_weight(co, affinity_pairs(sel_h, 4)) == 3
+    assert matching_weight(co, max_coselection_pairs(sel_h, 4)) == 4
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_greedy_is_within_half_of_the_maximum(seed):
+    # the greedy matching of a weight order is a 1/2-approximation of the maximum weight
+    from oracle.dense_union import affinity_pairs, matching_weight, max_coselection_pairs
+    inp = tiny_problem(T=256, P=16, S=6, seed=seed)
+    for h in range(2):
+        sel_h = inp["sel_pages"][h]
+        co = coselection(sel_h, 16)
+        g = matching_weight(co, affinity_pairs(sel_h, 16))
+        m = matching_weight(co, max_coselection_pairs(sel_h, 16))
+        assert _is_matching(max_coselection_pairs(sel_h, 16), 16)
+        assert m >= g >= m / 2
+
+
+def test_max_matching_merges_to_the_per_query_result():
+    from oracle.dense_union import max_coselection_pairs
+    inp = tiny_problem(T=128, P=16, Hq=4, Hkv=2, D=16, S=5, seed=4)
+    pb = _pb(inp)
+    pairing = {h: max_coselection_pairs(inp["sel_pages"][h], pb.N) for h in range(2)}
+    np.testing.assert_allclose(dense_union(pb, pairing), attention(pb), rtol=0, atol=1e-12)
