@@ -266,9 +266,25 @@ def dense_arms(pw, torch, wl, inp, dev, shp, O, calls, cold_ms, F_u):
     return arms
 
 
+def ordered_stages(pw, torch, wl, shp, q, k, v, sc, sel, ws, O):
+    """The complete call with each KV head's groups run by ascending union size
+    (pw_group_ordered + pw_tile_kv + pw_union_attention_tiled_ordered)."""
+    import ctypes
+    ids = torch.empty((wl.H_kv, wl.T), dtype=torch.int32, device="cuda")
+    order = torch.empty((wl.H_kv, -(-wl.T // wl.g)), dtype=torch.int32, device="cuda")
+    gws = torch.empty(max(1, int(pw._lib.pw_group_ordered_workspace_bytes(
+        ctypes.byref(shp), wl.W, wl.g))), dtype=torch.uint8, device="cuda")
+    return [lambda: pw.pw_group_ordered(shp, sel, wl.W, wl.g, query_ids=ids, group_order=order,
+                                        workspace=gws),
+            lambda: pw.pw_tile_kv(shp, k, v, sc, workspace=ws),
+            lambda: pw.pw_union_attention_tiled(shp, q, sel, ids, wl.g, ws, O=O,
+                                                group_order=order)]
+
+
 def selector_arm(pw, torch, wl, dev, shp, O, ws, ident, cold_ms):
     """The synthetic GPU selector (sink + 2 local pages + top pages by block key sums) and the
-    complete call on its selections, regrouped and with identity grouping (cold calls)."""
+    complete call on its selections, regrouped (the search's group order, and the groups run
+    by ascending union size) and with identity grouping (cold calls)."""
     sws = torch.empty(pw.pw_select_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
     sel = torch.empty_like(dev["sel_pages"])
     ids = torch.empty((wl.H_kv, wl.T), dtype=torch.int32, device="cuda")
@@ -279,16 +295,23 @@ def selector_arm(pw, torch, wl, dev, shp, O, ws, ident, cold_ms):
     attn = lambda idv: (lambda: pw.pw_union_attention_tiled(shp, q, sel, idv, wl.g, ws, O=O))
     sel_ms = cold_ms([select])
     select()
-    call_ms = cold_ms([search, tile, attn(ids)])
-    ident_ms = cold_ms([tile, attn(ident)])
+    ordered = ordered_stages(pw, torch, wl, shp, q, k, v, sc, sel, ws, O)
+    call_ms, ordered_ms, ident_ms = [], [], []
+    for _ in range(2):                   # alternated, so that drift hits every arm alike
+        call_ms.append(cold_ms([search, tile, attn(ids)], n=4))
+        ordered_ms.append(cold_ms(ordered, n=4))
+        ident_ms.append(cold_ms([tile, attn(ident)], n=4))
+    call_ms, ordered_ms, ident_ms = (float(np.median(x)) for x in (call_ms, ordered_ms, ident_ms))
     sel_np = sel.cpu().numpy()
     u = union_stats(sel_np, ids.cpu().numpy(), wl.g, wl.N)
     ui = union_stats(sel_np, ident.cpu().numpy(), wl.g, wl.N)
     del sws
-    return {"select_ms": sel_ms, "call_ms": call_ms, "identity_call_ms": ident_ms,
+    return {"select_ms": sel_ms, "call_ms": call_ms, "size_ordered_call_ms": ordered_ms,
+            "identity_call_ms": ident_ms,
             "regroup_gain_vs_identity": ident_ms / call_ms,
-            "union_pages_mean": float(u.mean()), "identity_union_pages_mean": float(ui.mean()),
-            "n_local": 2}
+            "size_ordered_regroup_gain_vs_identity": ident_ms / ordered_ms,
+            "union_pages_mean": float(u.mean()), "union_pages_std": float(u.std()),
+            "identity_union_pages_mean": float(ui.mean()), "n_local": 2}
 
 
 def cpu_model() -> str:
@@ -431,6 +454,8 @@ def main():
             arms[name] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12,
                           "union_pages_mean": float(us.mean()), "union_pages_total": int(us.sum())}
         arms["regroup_gain_vs_identity"] = arms["identity_union8"]["ms"] / ms_per_step
+        ms = cold_ms(ordered_stages(pw, torch, wl, shp, q, k, v, sc, sel, ws, O), n=10)
+        arms["regrouped_size_order"] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12}
         arms.update(dense_arms(pw, torch, wl, inp, dev, shp, O, calls, cold_ms, F_u))
         arms["selector"] = selector_arm(pw, torch, wl, dev, shp, O, ws, ident, cold_ms)
         arms["head_pipeline"] = head_pipeline_arm(pw, torch, wl, dev, shp, O, ws)

@@ -119,6 +119,28 @@ pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W,
                    void* stream);
 
 /* ---------------------------------------------------------------------------
+ * pw_group_ordered -- pw_group plus an execution order of the groups.
+ *
+ * [abs]: query unions share page loads.  The groups that the attention runs
+ * side by side also share pages through the caches when they sweep their
+ * ascending page lists in step, which happens when their unions have similar
+ * sizes.  The search knows every union it builds, so it also emits an order:
+ * per KV head, the group indices 0 .. ceil(T/g) - 1 by ascending union size
+ * (the number of distinct pages the members select), equal sizes in
+ * increasing index.  pw_union_attention_tiled_ordered runs the groups listed
+ * last first (largest unions first).
+ *
+ * In : as pw_group.  Out: query_ids int32 [H_kv][T], identical to pw_group's;
+ *      group_order int32 [H_kv][ceil(T/g)] (device).
+ * Workspace: pw_group_ordered_workspace_bytes() = H_kv * ceil(T/g) * 4 bytes
+ * (the union sizes), required.  Support set and errors as pw_group.
+ * ------------------------------------------------------------------------- */
+size_t pw_group_ordered_workspace_bytes(const pw_shape* shape, int32_t W, int32_t g);
+pw_status pw_group_ordered(const pw_shape* shape, const int32_t* sel_pages, int32_t W,
+                           int32_t g, int32_t* query_ids, int32_t* group_order, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * pw_check_ids -- is every query_ids row a permutation of 0..T-1?
  *
  * pw_union_attention writes exactly the rows listed in query_ids; with a row
@@ -245,6 +267,24 @@ pw_status pw_union_attention_tiled(const pw_shape* shape, const uint16_t* Q,
                                    const int32_t* sel_pages, const int32_t* query_ids,
                                    int32_t g, uint16_t* O, const void* ws, size_t ws_bytes,
                                    void* stream);
+
+/* ---------------------------------------------------------------------------
+ * pw_union_attention_tiled_ordered -- pw_union_attention_tiled with each KV
+ * head's groups run in a given order.
+ *
+ * [abs]: query unions share page loads (see pw_group_ordered for the order).
+ * group_order int32 [H_kv][ceil(T/g)] (device): per KV head a permutation of
+ * the group indices, e.g. from pw_group_ordered; the entries listed last run
+ * first.  An entry outside [0, ceil(T/g)) runs no group, so a row that is not
+ * a permutation leaves the output rows of the groups it misses unwritten.
+ * The output does not depend on the order: it equals
+ * pw_union_attention_tiled's bit for bit.  Other arguments, workspace and
+ * errors as pw_union_attention_tiled.
+ * ------------------------------------------------------------------------- */
+pw_status pw_union_attention_tiled_ordered(const pw_shape* shape, const uint16_t* Q,
+                                           const int32_t* sel_pages, const int32_t* query_ids,
+                                           const int32_t* group_order, int32_t g, uint16_t* O,
+                                           const void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
  * pw_union_attention_heads -- pw_union_attention for KV heads
@@ -387,7 +427,7 @@ const char* pw_last_error(void);
 /* ABI version of this header, PW_ABI_VERSION. */
 int32_t pw_abi_version(void);
 
-#define PW_ABI_VERSION 2
+#define PW_ABI_VERSION 3
 
 #ifdef __cplusplus
 }

@@ -89,10 +89,8 @@ int32_t pw_abi_version(void) { return PW_ABI_VERSION; }
 
 size_t pw_group_workspace_bytes(const pw_shape*, int32_t, int32_t) { return 0; }
 
-pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W, int32_t g,
-                   int32_t* query_ids, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
+static pw_status check_group_args(const pw_shape* shape, const int32_t* sel_pages, int32_t W,
+                                  int32_t g, const int32_t* query_ids) {
   pw_status st = check_shape(shape);
   if (st != PW_OK) return st;
   if (!sel_pages || !query_ids) return fail(PW_ERR_NULL, "sel_pages and query_ids are required");
@@ -103,8 +101,39 @@ pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W, i
                 "W = %d is not a multiple of g = %d (attention groups would straddle windows)", W, g);
   if (shape->N_pages > 1024)
     return fail(PW_ERR_UNSUPPORTED, "N_pages = %d exceeds 1024 for the search", shape->N_pages);
+  return PW_OK;
+}
+
+pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W, int32_t g,
+                   int32_t* query_ids, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  pw_status st = check_group_args(shape, sel_pages, W, g, query_ids);
+  if (st != PW_OK) return st;
   return hip_status(pw::launch_group(*shape, sel_pages, W, g, query_ids, (hipStream_t)stream),
                     "pw_group launch");
+}
+
+size_t pw_group_ordered_workspace_bytes(const pw_shape* shape, int32_t W, int32_t g) {
+  (void)W;
+  if (check_shape(shape) != PW_OK || g < 1) return 0;
+  return (size_t)shape->H_kv * ((shape->T + g - 1) / g) * sizeof(int32_t);
+}
+
+pw_status pw_group_ordered(const pw_shape* shape, const int32_t* sel_pages, int32_t W, int32_t g,
+                           int32_t* query_ids, int32_t* group_order, void* ws, size_t ws_bytes,
+                           void* stream) {
+  pw_status st = check_group_args(shape, sel_pages, W, g, query_ids);
+  if (st != PW_OK) return st;
+  if (!group_order) return fail(PW_ERR_NULL, "group_order is required");
+  const size_t need = pw_group_ordered_workspace_bytes(shape, W, g);
+  if (!ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
+  if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  int32_t* usize = static_cast<int32_t*>(ws);
+  hipError_t e = pw::launch_group(*shape, sel_pages, W, g, query_ids, (hipStream_t)stream, usize);
+  if (e != hipSuccess) return hip_status(e, "pw_group_ordered search launch");
+  return hip_status(pw::launch_group_order(*shape, g, usize, group_order, (hipStream_t)stream),
+                    "pw_group_ordered order launch");
 }
 
 size_t pw_check_ids_workspace_bytes(const pw_shape* shape) {
@@ -213,9 +242,10 @@ pw_status pw_tile_kv(const pw_shape* shape, const uint8_t* K_fp8, const uint8_t*
                     "pw_tile_kv launch");
 }
 
-pw_status pw_union_attention_tiled(const pw_shape* shape, const uint16_t* Q,
-                                   const int32_t* sel_pages, const int32_t* query_ids, int32_t g,
-                                   uint16_t* O, const void* ws, size_t ws_bytes, void* stream) {
+static pw_status tiled_attention(const pw_shape* shape, const uint16_t* Q,
+                                 const int32_t* sel_pages, const int32_t* query_ids,
+                                 const int32_t* group_order, int32_t g, uint16_t* O,
+                                 const void* ws, size_t ws_bytes, void* stream, const char* what) {
   pw_status st = check_shape(shape);
   if (st != PW_OK) return st;
   if (!Q || !sel_pages || !query_ids || !O)
@@ -225,8 +255,25 @@ pw_status pw_union_attention_tiled(const pw_shape* shape, const uint16_t* Q,
   st = check_tiled_workspace(shape, ws, ws_bytes);
   if (st != PW_OK) return st;
   return hip_status(pw::launch_union_attention_tiled(*shape, Q, sel_pages, query_ids, g, 0,
-                                                     shape->H_kv, O, ws, (hipStream_t)stream),
-                    "pw_union_attention_tiled launch");
+                                                     shape->H_kv, O, ws, (hipStream_t)stream,
+                                                     group_order),
+                    what);
+}
+
+pw_status pw_union_attention_tiled(const pw_shape* shape, const uint16_t* Q,
+                                   const int32_t* sel_pages, const int32_t* query_ids, int32_t g,
+                                   uint16_t* O, const void* ws, size_t ws_bytes, void* stream) {
+  return tiled_attention(shape, Q, sel_pages, query_ids, nullptr, g, O, ws, ws_bytes, stream,
+                         "pw_union_attention_tiled launch");
+}
+
+pw_status pw_union_attention_tiled_ordered(const pw_shape* shape, const uint16_t* Q,
+                                           const int32_t* sel_pages, const int32_t* query_ids,
+                                           const int32_t* group_order, int32_t g, uint16_t* O,
+                                           const void* ws, size_t ws_bytes, void* stream) {
+  if (!group_order) return fail(PW_ERR_NULL, "group_order is required");
+  return tiled_attention(shape, Q, sel_pages, query_ids, group_order, g, O, ws, ws_bytes, stream,
+                         "pw_union_attention_tiled_ordered launch");
 }
 
 size_t pw_dense_union_ref_workspace_bytes(const pw_shape* shape) {

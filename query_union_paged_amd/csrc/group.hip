@@ -55,7 +55,8 @@ __device__ __forceinline__ uint32_t wave_min_dpp(uint32_t v) {
 template <int C, int NWB, int NWV>
 __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, int S, int N,
                                             int Wr, int g, const uint16_t* rank,
-                                            uint32_t* stage, int* order, uint32_t* xch) {
+                                            uint32_t* stage, int* order, uint32_t* xch,
+                                            int32_t* __restrict__ usz) {
   const int lane = threadIdx.x & 63;
   const int wv = NWV > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
   static_assert(NWV == 1 || (C & (C - 1)) == 0, "several waves need C in {1, 2, 4}");
@@ -164,7 +165,7 @@ __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, i
     for (int c = 0; c < C; ++c) gain[c] += __builtin_popcount(b[c][jj] & delta);
   };
 
-  int pos = 0;
+  int pos = 0, grp = 0;
   while (pos < Wr) {
     // ---- seed: the lowest unassigned ID owns the next group
     uint32_t key = kNone;
@@ -208,6 +209,14 @@ __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, i
         }
       }
     }
+    // ---- the closed group's union size (pages), when the caller asks for it
+    if (usz != nullptr) {
+      int n = 0;
+#pragma unroll
+      for (int jj = 0; jj < NWB; ++jj) n += __builtin_popcount(U[jj]);
+      if (wv == 0 && lane == 0) usz[grp] = n;
+    }
+    ++grp;
   }
 }
 
@@ -216,7 +225,8 @@ __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, i
 template <int C, int NWV>
 __global__ __launch_bounds__(64 * NWV) void group_kernel(const int32_t* __restrict__ sel,
                                                          int32_t* __restrict__ ids, int T, int S,
-                                                         int N, int W, int g, int n_windows) {
+                                                         int N, int W, int g, int n_windows,
+                                                         int32_t* __restrict__ usize) {
   extern __shared__ uint32_t lds[];
   const int lane = threadIdx.x & 63;
   const int wv = NWV > 1 ? __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) : 0;
@@ -230,6 +240,8 @@ __global__ __launch_bounds__(64 * NWV) void group_kernel(const int32_t* __restri
   const int w0 = (blockIdx.x % n_windows) * W;
   const int Wr = min(W, T - w0);
   const int32_t* wbase = sel + ((size_t)h * T + w0) * S;
+  // union sizes of this window's groups (W is a multiple of g: they start at group w0 / g)
+  int32_t* usz = usize != nullptr ? usize + (size_t)h * ((T + g - 1) / g) + w0 / g : nullptr;
   // this wave's candidate rows
   const int r_lo = min(Wr, 64 * C * wv), r_hi = min(Wr, 64 * C * (wv + 1));
 
@@ -240,7 +252,7 @@ __global__ __launch_bounds__(64 * NWV) void group_kernel(const int32_t* __restri
     if constexpr (NWV > 1) __syncthreads(); else wave_sync();
   };
   if (N <= 256) {            // every page fits in 8 words: pages are their own ranks
-    window_body<C, 8, NWV>(wbase, S, N, Wr, g, nullptr, stage, order, xch);
+    window_body<C, 8, NWV>(wbase, S, N, Wr, g, nullptr, stage, order, xch, usz);
     sync();
     for (int i = threadIdx.x; i < Wr; i += 64 * NWV) ids[(size_t)h * T + w0 + i] = w0 + order[i];
     return;
@@ -287,38 +299,146 @@ __global__ __launch_bounds__(64 * NWV) void group_kernel(const int32_t* __restri
     rank[u] = (uint16_t)(wpre[u >> 5] + __builtin_popcount(apg[u >> 5] & ((1u << (u & 31)) - 1u)));
   sync();
   if (n_act <= 256)
-    window_body<C, 8, NWV>(wbase, S, N, Wr, g, rank, stage, order, xch);
+    window_body<C, 8, NWV>(wbase, S, N, Wr, g, rank, stage, order, xch, usz);
   else if (n_act <= 512)
-    window_body<C, 16, NWV>(wbase, S, N, Wr, g, rank, stage, order, xch);
+    window_body<C, 16, NWV>(wbase, S, N, Wr, g, rank, stage, order, xch, usz);
   else
-    window_body<C, 32, NWV>(wbase, S, N, Wr, g, rank, stage, order, xch);
+    window_body<C, 32, NWV>(wbase, S, N, Wr, g, rank, stage, order, xch, usz);
   sync();
   for (int i = threadIdx.x; i < Wr; i += 64 * NWV) ids[(size_t)h * T + w0 + i] = w0 + order[i];
 }
 
 template <int C, int NWV>
 hipError_t launch_c(const pw_shape& s, const int32_t* sel, int W, int g, int32_t* ids,
-                    hipStream_t stream) {
+                    int32_t* usize, hipStream_t stream) {
   const int n_windows = (s.T + W - 1) / W;
   const size_t lds =
       ((size_t)NWV * 64 * kStride + (size_t)NWV * C * 64 + 36 + 32 + 32) * 4 + (size_t)s.N_pages * 2;
   hipLaunchKernelGGL((group_kernel<C, NWV>), dim3(s.H_kv * n_windows), dim3(64 * NWV), lds,
-                     stream, sel, ids, s.T, s.S, s.N_pages, W, g, n_windows);
+                     stream, sel, ids, s.T, s.S, s.N_pages, W, g, n_windows, usize);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_group(const pw_shape& s, const int32_t* sel, int W, int g, int32_t* ids,
-                        hipStream_t stream) {
+                        hipStream_t stream, int32_t* usize) {
   const int C = (W + 63) / 64;
-  if (C <= 1) return launch_c<1, 1>(s, sel, W, g, ids, stream);
-  if (C == 2) return launch_c<2, 1>(s, sel, W, g, ids, stream);
-  if (C == 3) return launch_c<3, 1>(s, sel, W, g, ids, stream);
-  if (C == 4) return launch_c<4, 1>(s, sel, W, g, ids, stream);
-  if (W <= 512) return launch_c<4, 2>(s, sel, W, g, ids, stream);
-  if (W <= 768) return launch_c<4, 3>(s, sel, W, g, ids, stream);
-  return launch_c<4, 4>(s, sel, W, g, ids, stream);
+  if (C <= 1) return launch_c<1, 1>(s, sel, W, g, ids, usize, stream);
+  if (C == 2) return launch_c<2, 1>(s, sel, W, g, ids, usize, stream);
+  if (C == 3) return launch_c<3, 1>(s, sel, W, g, ids, usize, stream);
+  if (C == 4) return launch_c<4, 1>(s, sel, W, g, ids, usize, stream);
+  if (W <= 512) return launch_c<4, 2>(s, sel, W, g, ids, usize, stream);
+  if (W <= 768) return launch_c<4, 3>(s, sel, W, g, ids, usize, stream);
+  return launch_c<4, 4>(s, sel, W, g, ids, usize, stream);
+}
+
+// ---- execution order of the groups: per KV head, the groups by ascending
+// union size, equal sizes in index order (a stable counting sort).  One
+// workgroup of 16 waves per KV head; wave w owns a contiguous segment of the
+// head's groups.  The waves count their segments' sizes into per-wave LDS
+// histograms; an exclusive scan over (size, wave) turns those into the first
+// output position of every (wave, size); each wave then walks its segment 64
+// groups at a time in index order, the lanes holding equal sizes finding each
+// other with eleven ballots (one per bit of the size), so positions follow
+// the index order without atomics.
+namespace {
+
+constexpr int kMaxUnion = 1024;          // union sizes are at most N_pages <= 1024
+constexpr int kKeys = kMaxUnion + 1;
+constexpr int kOrderWaves = 16;
+
+__global__ __launch_bounds__(64 * kOrderWaves) void group_order_kernel(
+    const int32_t* __restrict__ usize, int ngroups, int32_t* __restrict__ order) {
+  __shared__ int cnt[kOrderWaves][kKeys];
+  __shared__ int wsum[kOrderWaves];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t* sz = usize + (size_t)blockIdx.x * ngroups;
+  int32_t* out = order + (size_t)blockIdx.x * ngroups;
+  const int seg = (ngroups + kOrderWaves - 1) / kOrderWaves;
+  const int s0 = min(ngroups, wave * seg), s1 = min(ngroups, s0 + seg);
+  auto key_of = [&](int i) __attribute__((always_inline)) {
+    return min(max((int)sz[i], 0), kMaxUnion);
+  };
+  for (int i = tid; i < kOrderWaves * kKeys; i += 64 * kOrderWaves) (&cnt[0][0])[i] = 0;
+  __syncthreads();
+  // per-wave histograms of the segments (8 loads in flight per lane)
+  for (int i0 = s0; i0 < s1; i0 += 64 * 8) {
+    int k[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + 64 * j + lane;
+      k[j] = i < s1 ? key_of(i) : -1;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (k[j] >= 0) atomicAdd(&cnt[wave][k[j]], 1);
+  }
+  __syncthreads();
+  // exclusive scan over keys of the totals (thread t: key t; the positions of the last
+  // key, 1024, follow those of key 1023 and are set by thread 1023)
+  constexpr int kT = 64 * kOrderWaves;
+  static_assert(kT == kKeys - 1, "one key per thread plus the last");
+  int tot = 0;
+#pragma unroll
+  for (int w = 0; w < kOrderWaves; ++w) tot += cnt[w][tid];
+  int incl = tot;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int w = 0; w < wave; ++w) before += wsum[w];
+  int off = before + incl - tot;                       // first position of key tid
+  // first position of every (wave, key): keys ascending, waves in index order
+#pragma unroll
+  for (int w = 0; w < kOrderWaves; ++w) {
+    const int c = cnt[w][tid];
+    cnt[w][tid] = off;
+    off += c;
+  }
+  if (tid == kT - 1) {                                  // key kMaxUnion follows key 1023
+#pragma unroll
+    for (int w = 0; w < kOrderWaves; ++w) {
+      const int c = cnt[w][kMaxUnion];
+      cnt[w][kMaxUnion] = off;
+      off += c;
+    }
+  }
+  __syncthreads();
+  // stable placement within each wave's segment
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int i0 = s0; i0 < s1; i0 += 64) {
+    const int i = i0 + lane;
+    const bool live = i < s1;
+    const int key = live ? key_of(i) : 0;
+    uint64_t eq = __ballot(live);
+#pragma unroll
+    for (int b = 0; b < 11; ++b) {
+      const uint64_t m = __ballot((key >> b) & 1);
+      eq &= ((key >> b) & 1) ? m : ~m;
+    }
+    const int pos = live ? cnt[wave][key] + __popcll(eq & below) : 0;
+    wave_sync();
+    if (live) {
+      out[pos] = i;
+      if ((eq >> lane) == 1ull) cnt[wave][key] += __popcll(eq);   // the highest lane of its size
+    }
+    wave_sync();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_group_order(const pw_shape& s, int g, const int32_t* usize, int32_t* order,
+                              hipStream_t stream) {
+  const int ngroups = (s.T + g - 1) / g;
+  hipLaunchKernelGGL(group_order_kernel, dim3(s.H_kv), dim3(64 * kOrderWaves), 0, stream, usize,
+                     ngroups, order);
+  return hipGetLastError();
 }
 
 }  // namespace pw

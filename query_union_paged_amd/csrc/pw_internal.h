@@ -39,8 +39,12 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 }
 
 // Host-side launchers (implemented next to their kernels).
+// usize (optional): the union size of every group, int32 [H_kv][ceil(T / g)]
 hipError_t launch_group(const pw_shape& s, const int32_t* sel, int W, int g, int32_t* ids,
-                        hipStream_t stream);
+                        hipStream_t stream, int32_t* usize = nullptr);
+// Per KV head, the groups by ascending union size (equal sizes in index order).
+hipError_t launch_group_order(const pw_shape& s, int g, const int32_t* usize, int32_t* order,
+                              hipStream_t stream);
 // FP8 K/V pages re-tiled in MFMA operand order (K tiles, then V tiles), then
 // 16 bytes of softmax factors per (page, KV head).
 size_t tiled_kv_bytes(const pw_shape& s);
@@ -53,9 +57,12 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
                                   uint16_t* O, void* ws, hipStream_t stream);
 // The attention alone, on a workspace that tile_kv has filled for heads
 // h_begin .. h_begin + h_count - 1.
+// order (optional): per KV head, the execution order of its groups (a
+// permutation of 0 .. ceil(T / g) - 1, the last entries run first).
 hipError_t launch_union_attention_tiled(const pw_shape& s, const uint16_t* Q, const int32_t* sel,
                                         const int32_t* ids, int g, int h_begin, int h_count,
-                                        uint16_t* O, const void* ws, hipStream_t stream);
+                                        uint16_t* O, const void* ws, hipStream_t stream,
+                                        const int32_t* order = nullptr);
 hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* tiles,
                                  const float* scales, const int2* plist, const int* pcount,
                                  const int* tstart, const int2* pairs, int tiles_head,

@@ -59,6 +59,7 @@ struct UAParams {
   uint16_t* O;
   int T, Hq, Hkv, G, P, N, S, g;
   int groups_per_head, total_groups;
+  const int32_t* order;  // optional [H_kv][groups_per_head]: execution order of each head's groups
   int h_begin;       // first KV head of the call (groups cover heads h_begin ...)
   int n_rt;          // 32-row tiles per group (ceil(g * G / 32)): one wave each
   int total_items;   // total_groups * n_rt
@@ -216,7 +217,12 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   if constexpr (MODE == kUnionMode) {
   const int hl = gid / p.groups_per_head;
   h = p.h_begin + hl;
-  const int g0 = (gid - hl * p.groups_per_head) * p.g;
+  int k = gid - hl * p.groups_per_head;
+  if (p.order != nullptr) {
+    k = p.order[(size_t)h * p.groups_per_head + k];
+    if (k < 0 || k >= p.groups_per_head) return;       // not a group index: nothing to run
+  }
+  const int g0 = k * p.g;
   gm = min(p.g, p.T - g0);
   const int nw = (p.N + 31) >> 5;              // words of the page bitset
   uint32_t* bits = reinterpret_cast<uint32_t*>(wbase + (size_t)p.n_umax * 4);
@@ -469,7 +475,8 @@ hipError_t tile_kv(const pw_shape& s, const uint8_t* K, const uint8_t* V, const 
 
 hipError_t launch_union_attention_tiled(const pw_shape& s, const uint16_t* Q, const int32_t* sel,
                                         const int32_t* ids, int g, int h_begin, int h_count,
-                                        uint16_t* O, const void* ws, hipStream_t stream) {
+                                        uint16_t* O, const void* ws, hipStream_t stream,
+                                        const int32_t* order) {
   const uint8_t* tiles = static_cast<const uint8_t*>(ws);
   UAParams prm;
   common_params(prm, s, Q, nullptr);
@@ -478,6 +485,7 @@ hipError_t launch_union_attention_tiled(const pw_shape& s, const uint16_t* Q, co
   prm.pf = reinterpret_cast<const float4*>(tiles + tiled_pf_offset(s));
   prm.sel = sel; prm.ids = ids; prm.O = O; prm.g = g;
   prm.groups_per_head = (s.T + g - 1) / g;
+  prm.order = order;
   prm.total_groups = prm.groups_per_head * h_count;
   prm.h_begin = h_begin;
   prm.n_umax = (g * s.S < s.N_pages) ? g * s.S : s.N_pages;

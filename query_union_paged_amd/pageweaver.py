@@ -46,6 +46,8 @@ _SHP = ctypes.POINTER(PWShape)
 _SIGS = {
     "pw_group_workspace_bytes": (_sz, [_SHP, _i32, _i32]),
     "pw_group": (_i32, [_SHP, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "pw_group_ordered_workspace_bytes": (_sz, [_SHP, _i32, _i32]),
+    "pw_group_ordered": (_i32, [_SHP, _vp, _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "pw_union_attention_workspace_bytes": (_sz, [_SHP, _i32]),
     "pw_union_attention": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "pw_union_attention_heads": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp,
@@ -53,6 +55,8 @@ _SIGS = {
     "pw_union_attention_noalloc": (_i32, [_SHP, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp]),
     "pw_tile_kv": (_i32, [_SHP, _vp, _vp, _vp, _vp, _sz, _vp]),
     "pw_union_attention_tiled": (_i32, [_SHP, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
+    "pw_union_attention_tiled_ordered": (_i32, [_SHP, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz,
+                                                _vp]),
     "pw_check_ids_workspace_bytes": (_sz, [_SHP]),
     "pw_check_ids": (_i32, [_SHP, _vp, _vp, _vp, _sz, _vp]),
     "pw_select_workspace_bytes": (_sz, [_SHP]),
@@ -122,6 +126,29 @@ def pw_group(shp: PWShape, sel_pages: torch.Tensor, W: int, g: int,
     ids = _dev(query_ids, "query_ids", (torch.int32,), (shp.H_kv, shp.T))
     _check(_lib.pw_group(ctypes.byref(shp), sel, W, g, ids, None, 0, _stream(stream)), "pw_group")
     return query_ids
+
+
+def pw_group_ordered(shp: PWShape, sel_pages: torch.Tensor, W: int, g: int,
+                     query_ids: Optional[torch.Tensor] = None,
+                     group_order: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None, stream=None):
+    """pw_group plus each KV head's groups by ascending union size; returns (query_ids,
+    group_order)."""
+    sel = _dev(sel_pages, "sel_pages", (torch.int32,), (shp.H_kv, shp.T, shp.S))
+    ng = (shp.T + g - 1) // g if g > 0 else 0
+    if query_ids is None:
+        query_ids = torch.empty((shp.H_kv, shp.T), dtype=torch.int32, device=sel_pages.device)
+    if group_order is None:
+        group_order = torch.empty((shp.H_kv, ng), dtype=torch.int32, device=sel_pages.device)
+    if workspace is None:
+        workspace = torch.empty(max(1, int(_lib.pw_group_ordered_workspace_bytes(
+            ctypes.byref(shp), W, g))), dtype=torch.uint8, device=sel_pages.device)
+    ids = _dev(query_ids, "query_ids", (torch.int32,), (shp.H_kv, shp.T))
+    order = _dev(group_order, "group_order", (torch.int32,), (shp.H_kv, ng))
+    ws = _dev(workspace, "workspace", (torch.uint8,))
+    _check(_lib.pw_group_ordered(ctypes.byref(shp), sel, W, g, ids, order, ws, workspace.numel(),
+                                 _stream(stream)), "pw_group_ordered")
+    return query_ids, group_order
 
 
 def pw_union_attention_workspace_bytes(shp: PWShape, g: int = 8) -> int:
@@ -200,8 +227,10 @@ def pw_tile_kv(shp: PWShape, K_fp8, V_fp8, scales, workspace: Optional[torch.Ten
 
 def pw_union_attention_tiled(shp: PWShape, Q, sel_pages, query_ids, g: int,
                              workspace: torch.Tensor, O: Optional[torch.Tensor] = None,
-                             stream=None) -> torch.Tensor:
-    """Union attention on a workspace that pw_tile_kv filled for the same K/V."""
+                             stream=None, group_order: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Union attention on a workspace that pw_tile_kv filled for the same K/V; with
+    `group_order` (from pw_group_ordered) the groups run in that order
+    (pw_union_attention_tiled_ordered)."""
     T, Hq, Hkv, D, S = shp.T, shp.H_q, shp.H_kv, shp.D, shp.S
     q = _dev(Q, "Q", _BF16, (T, Hq, D))
     sel = _dev(sel_pages, "sel_pages", (torch.int32,), (Hkv, T, S))
@@ -210,9 +239,15 @@ def pw_union_attention_tiled(shp: PWShape, Q, sel_pages, query_ids, g: int,
         O = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=Q.device)
     o = _dev(O, "O", _BF16, (T, Hq, D))
     ws = _dev(workspace, "workspace", (torch.uint8,))
-    _check(_lib.pw_union_attention_tiled(ctypes.byref(shp), q, sel, ids, g, o, ws,
-                                         workspace.numel(), _stream(stream)),
-           "pw_union_attention_tiled")
+    if group_order is None:
+        _check(_lib.pw_union_attention_tiled(ctypes.byref(shp), q, sel, ids, g, o, ws,
+                                             workspace.numel(), _stream(stream)),
+               "pw_union_attention_tiled")
+    else:
+        order = _dev(group_order, "group_order", (torch.int32,), (Hkv, (T + g - 1) // g))
+        _check(_lib.pw_union_attention_tiled_ordered(ctypes.byref(shp), q, sel, ids, order, g, o,
+                                                     ws, workspace.numel(), _stream(stream)),
+               "pw_union_attention_tiled_ordered")
     return O
 
 

@@ -20,7 +20,7 @@ def test_every_declared_symbol_is_exported():
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     missing = [n for n in names if n not in exported]
     assert not missing, missing
-    assert pw._lib.pw_abi_version() == 2
+    assert pw._lib.pw_abi_version() == 3
 
 
 def test_status_strings():
@@ -104,6 +104,26 @@ def test_tiled_validation():
     big = _shape(T=4096 * 16, N_pages=4096, H_q=64, H_kv=64, D=128)
     assert t(ctypes.byref(big), FAKE, FAKE, FAKE, ws, 1 << 40, None) == pw.PW_ERR_UNSUPPORTED
     assert b"2 GiB" in pw._lib.pw_last_error()
+
+
+def test_ordered_validation():
+    # pw_group_ordered: the pw_group checks, then the order output and the union-size workspace
+    shp = _shape()
+    need = pw._lib.pw_group_ordered_workspace_bytes(ctypes.byref(shp), 32, 8)
+    assert need == 1 * (1024 // 8) * 4
+    ws = ctypes.c_void_p(0x100000)
+    go = pw._lib.pw_group_ordered
+    assert go(None, FAKE, 32, 8, FAKE, FAKE, ws, need, None) == pw.PW_ERR_NULL
+    assert go(ctypes.byref(shp), FAKE, 36, 8, FAKE, FAKE, ws, need, None) == pw.PW_ERR_UNSUPPORTED
+    assert go(ctypes.byref(shp), FAKE, 32, 8, FAKE, None, ws, need, None) == pw.PW_ERR_NULL
+    assert go(ctypes.byref(shp), FAKE, 32, 8, FAKE, FAKE, None, need, None) == pw.PW_ERR_NULL
+    assert go(ctypes.byref(shp), FAKE, 32, 8, FAKE, FAKE, ws, need - 1, None) == pw.PW_ERR_WORKSPACE
+    # pw_union_attention_tiled_ordered: the tiled checks plus a required order
+    wneed = pw._lib.pw_union_attention_workspace_bytes(ctypes.byref(shp), 8)
+    a = pw._lib.pw_union_attention_tiled_ordered
+    assert a(ctypes.byref(shp), FAKE, FAKE, FAKE, None, 8, FAKE, ws, wneed, None) == pw.PW_ERR_NULL
+    assert a(ctypes.byref(shp), FAKE, FAKE, FAKE, FAKE, 17, FAKE, ws, wneed, None) == pw.PW_ERR_UNSUPPORTED
+    assert a(ctypes.byref(shp), FAKE, FAKE, FAKE, FAKE, 8, FAKE, ws, wneed - 1, None) == pw.PW_ERR_WORKSPACE
 
 
 def test_noalloc_validation():

@@ -141,3 +141,48 @@ def test_check_ids_counts():
     want = [int(((r < 0) | (r >= wl.T)).sum()) + int(((r >= 0) & (r < wl.T)).sum()) -
             len(set(r[(r >= 0) & (r < wl.T)].tolist())) for r in b]
     assert got.tolist() == want == [0, 1, 0, 4, 0, 0, 0, 0]
+
+
+def _union_sizes(sel_np, ids, N, g):
+    """Distinct valid pages of every group's members, numpy, [H][ceil(T / g)]."""
+    H, T, _ = sel_np.shape
+    ng = -(-T // g)
+    out = np.zeros((H, ng), np.int64)
+    for h in range(H):
+        for k in range(ng):
+            rows = sel_np[h, ids[h, k * g:(k + 1) * g]]
+            out[h, k] = len(np.unique(rows[(rows >= 0) & (rows < N)]))
+    return out
+
+
+@pytest.mark.parametrize("case", ["prefill_8k", "rand256", "rand512_ragged", "wide1024"])
+def test_group_order(case):
+    # pw_group_ordered: the same IDs as pw_group, and per KV head the groups by ascending union
+    # size with equal sizes in index order (checked against sizes counted here with numpy)
+    pw = _pw()
+    log(f"[case] pw_group_ordered {case}")
+    if case == "prefill_8k":
+        wl = synth.WORKLOADS[case]
+        sel, N, P, W, g, Hq = host_inputs(case)["sel_pages"], wl.N, wl.P, wl.W, wl.g, wl.H_q
+    else:
+        rng = np.random.default_rng(len(case))
+        T, P = {"rand256": (1024, 4), "rand512_ragged": (1020, 2), "wide1024": (2048, 4)}[case]
+        N = T // P
+        W, g = {"rand256": (64, 8), "rand512_ragged": (300, 5), "wide1024": (1024, 8)}[case]
+        sel = rng.integers(-3, N + 3, size=(2, T, 12)).astype(np.int32)
+        sel[:, ::3] %= 24                    # clustered rows: many groups of equal union size
+        Hq = 2
+    H, T, S = sel.shape
+    shp = pw.shape(T, Hq, H, 128, P, N, S)
+    sel_d = torch.from_numpy(sel).cuda()
+    ids_plain = pw.pw_group(shp, sel_d, W, g)
+    ids, order = pw.pw_group_ordered(shp, sel_d, W, g)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, ids_plain)
+    ids_np, order_np = ids.cpu().numpy(), order.cpu().numpy()
+    sizes = _union_sizes(sel, ids_np, N, g)
+    ng = sizes.shape[1]
+    for h in range(H):
+        want = np.lexsort((np.arange(ng), sizes[h]))       # by size, then by index
+        assert np.array_equal(order_np[h], want), f"head {h}"
+    log(f"[parity] {case}: {ng} groups per head, union sizes {sizes.min()}..{sizes.max()}")

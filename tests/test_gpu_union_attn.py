@@ -374,3 +374,51 @@ def test_disjoint_head_ranges_share_a_workspace_concurrently():
         pw.pw_union_attention(*args, O=O, workspace=ws, stream=s2, heads=(4, 4))
     torch.cuda.synchronize()
     assert torch.equal(O.view(torch.int16), O_ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", ["prefill_8k", "shape_g8"])
+def test_group_order_leaves_every_row_unchanged(name):
+    # pw_union_attention_tiled_ordered: the search's size order, a random permutation and the
+    # plain order give bit-identical outputs; an order entry outside the group range runs no
+    # group (its rows keep their previous contents)
+    pw = _pw()
+    log(f"[case] ordered attention {name}")
+    if name == "prefill_8k":
+        wl = synth.WORKLOADS[name]
+        inp, g, W = host_inputs(name), wl.g, wl.W
+    else:                                   # G = 8: two 32-row tiles per group
+        inp, g, W = tiny_problem(T=2048, P=32, Hq=16, Hkv=2, D=128, S=10, seed=11), 8, 64
+    dev = pw.to_device(inp)
+    T, Hq, D = inp["q_bits"].shape
+    N, Hkv, P, _ = inp["k_codes"].shape
+    S = inp["sel_pages"].shape[2]
+    shp = pw.shape(T, Hq, Hkv, D, P, N, S)
+    ids, order = pw.pw_group_ordered(shp, dev["sel_pages"], W, g)
+    ws = pw.pw_tile_kv(shp, dev["k_codes"], dev["v_codes"], dev["scales"])
+    plain = pw.pw_union_attention_tiled(shp, dev["q_bits"], dev["sel_pages"], ids, g, ws)
+    sized = pw.pw_union_attention_tiled(shp, dev["q_bits"], dev["sel_pages"], ids, g, ws,
+                                        group_order=order)
+    ng = order.shape[1]
+    perm = torch.stack([torch.randperm(ng, generator=torch.Generator().manual_seed(h))
+                        for h in range(Hkv)]).to(torch.int32).cuda()
+    shuffled = pw.pw_union_attention_tiled(shp, dev["q_bits"], dev["sel_pages"], ids, g, ws,
+                                           group_order=perm)
+    torch.cuda.synchronize()
+    assert torch.equal(plain.view(torch.int16), sized.view(torch.int16))
+    assert torch.equal(plain.view(torch.int16), shuffled.view(torch.int16))
+    # group 3 of head 0 is replaced by an out-of-range entry: its rows stay as they were
+    bad = order.clone()
+    pos = int((bad[0] == 3).nonzero()[0, 0])
+    bad[0, pos] = ng
+    O = torch.full_like(plain, 7.0)
+    pw.pw_union_attention_tiled(shp, dev["q_bits"], dev["sel_pages"], ids, g, ws, O=O,
+                                group_order=bad)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    miss = ids[0, 3 * g:4 * g].long().cpu()
+    heads0 = slice(0, G)
+    assert torch.all(O[miss][:, heads0] == 7.0)
+    keep = torch.ones(T, dtype=torch.bool)
+    keep[miss] = False
+    assert torch.equal(O[keep].view(torch.int16), plain[keep].view(torch.int16))
+    assert torch.equal(O[miss][:, G:].view(torch.int16), plain[miss][:, G:].view(torch.int16))
