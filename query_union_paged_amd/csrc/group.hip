@@ -18,6 +18,9 @@
 // come to scalar registers by readlane; only the words where it brings new
 // pages (delta = B_best & ~U) touch the candidates, whose cost is kept as
 // |B_c| - |B_c & U| with |B_c & U| accumulated popcount by popcount.
+// On request the search also records each group's union size as it closes the
+// group; group_order_kernel (below) turns those sizes into an execution order
+// of the groups for the attention.
 #include "pw_internal.h"
 
 namespace pw {

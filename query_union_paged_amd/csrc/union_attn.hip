@@ -199,7 +199,10 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   // each XCD sweeps a contiguous range of groups (one KV head's pages stay in
   // that XCD's L2).
   // Each XCD takes its range from the top down: late queries have the largest
-  // supports, so the cheap early groups are the ones left for the tail.
+  // supports, so the cheap early groups are the ones left for the tail.  With a
+  // group order, sweep position k of a head runs group order[h][k] instead (the
+  // search's order by ascending union size: largest unions first, and unions of
+  // similar size side by side, whose ascending page sweeps stay in step).
   const int nb = gridDim.x, b = blockIdx.x;
   const int xcd = b & 7, per = nb >> 3, extra = nb & 7;
   const int cnt = per + (xcd < extra ? 1 : 0);       // workgroups of this XCD
