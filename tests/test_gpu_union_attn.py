@@ -376,7 +376,7 @@ def test_disjoint_head_ranges_share_a_workspace_concurrently():
     assert torch.equal(O.view(torch.int16), O_ref.view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["prefill_8k", "shape_g8"])
+@pytest.mark.parametrize("name", ["prefill_8k", "shape_g8", "ragged"])
 def test_group_order_leaves_every_row_unchanged(name):
     # pw_union_attention_tiled_ordered: the search's size order, a random permutation and the
     # plain order give bit-identical outputs; an order entry outside the group range runs no
@@ -386,8 +386,10 @@ def test_group_order_leaves_every_row_unchanged(name):
     if name == "prefill_8k":
         wl = synth.WORKLOADS[name]
         inp, g, W = host_inputs(name), wl.g, wl.W
-    else:                                   # G = 8: two 32-row tiles per group
+    elif name == "shape_g8":                # G = 8: two 32-row tiles per group
         inp, g, W = tiny_problem(T=2048, P=32, Hq=16, Hkv=2, D=128, S=10, seed=11), 8, 64
+    else:                                   # T = 1008, g = 5: the last group has 3 members
+        inp, g, W = tiny_problem(T=1008, P=16, Hq=8, Hkv=2, D=64, S=6, seed=5), 5, 35
     dev = pw.to_device(inp)
     T, Hq, D = inp["q_bits"].shape
     N, Hkv, P, _ = inp["k_codes"].shape
