@@ -131,8 +131,21 @@ def test_large_sampled(name, arms):
     for arm in arms:
         log(f"[case] union {name} arm={arm}")
         g = 1 if arm == "g1" else wl.g
-        O, _ = _run(inp, g, "identity" if arm == "identity" else "regroup", wl.W)
+        O, ids = _run(inp, g, "identity" if arm == "identity" else "regroup", wl.W)
         assert_close(gpu_rows(O, pairs, wl.G), ref, f"{name} {arm}")
+        if arm == "regroup":
+            # the same call with the search's size order: bit-identical rows
+            pw = _pw()
+            dev = pw.to_device(inp)
+            shp = pw.shape(*wl.shape_tuple())
+            ids_o, order = pw.pw_group_ordered(shp, dev["sel_pages"], wl.W, wl.g)
+            ws = pw.pw_tile_kv(shp, dev["k_codes"], dev["v_codes"], dev["scales"])
+            O_o = pw.pw_union_attention_tiled(shp, dev["q_bits"], dev["sel_pages"], ids_o, wl.g,
+                                              ws, group_order=order)
+            torch.cuda.synchronize()
+            assert torch.equal(ids_o, ids)
+            assert torch.equal(O_o.view(torch.int16), O.view(torch.int16))
+            del dev, ws, O_o
         del O
         torch.cuda.empty_cache()
 
