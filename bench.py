@@ -354,7 +354,7 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
-              "(the path shards by KV head with no communication; see the design notes).",
+              "(the path shards by KV head with no communication between GPUs).",
               file=sys.stderr)
         sys.exit(2)
     import torch

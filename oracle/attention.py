@@ -13,7 +13,7 @@ head h, query (token) t and Q head hq of h:
   s_j       = <Q[t][hq], K^(j)> / sqrt(D)
   O[t][hq]  = sum_j softmax(s)_j V^(j)        (O = 0 when J is empty)
 
-Readings where the pages are silent (each listed in the design notes):
+Readings where the pages are silent:
 softmax scale 1/sqrt(D); Q head hq belongs to KV head hq // G; query t sits at
 token t and sees key j iff j <= t (whole-context causal prefill); a slot value
 outside [0, N) is an empty slot and repeated pages count once (the support is

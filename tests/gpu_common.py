@@ -9,9 +9,10 @@ import torch
 from query_union_paged_amd import synth
 from oracle.attention import Problem, attention_pairs_parallel
 
-# The pages fix no numeric tolerance; the bound on the bf16 output is
-# max |O_gpu - O_oracle| <= 2e-2 and mean |O_gpu - O_oracle| <= 2e-3 over the
-# compared elements (derivation in the design notes).
+# Bound on the bf16 output: max |O_gpu - O_oracle| <= 2e-2 and
+# mean |O_gpu - O_oracle| <= 2e-3 over the compared elements.  The output's own
+# bf16 rounding contributes up to 2^-8 |O| (0.018 for |O| <= 4.5, the range of
+# the inputs' dequantised V), and the kernel's fp32 accumulation far less.
 TOL_MAX = 2e-2
 TOL_MEAN = 2e-3
 # relative RMS error ||dO|| / ||O|| over the compared rows: the bf16 rounding of the
