@@ -124,11 +124,14 @@ pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W,
  * [abs]: query unions share page loads.  The groups that the attention runs
  * side by side also share pages through the caches when they sweep their
  * ascending page lists in step, which happens when their unions have similar
- * sizes.  The search knows every union it builds, so it also emits an order:
- * per KV head, the group indices 0 .. ceil(T/g) - 1 by ascending union size
- * (the number of distinct pages the members select), equal sizes in
- * increasing index.  pw_union_attention_tiled_ordered runs the groups listed
- * last first (largest unions first).
+ * sizes and come from nearby queries.  The search knows every union it builds,
+ * so it also emits an order: per KV head, the group indices 0 .. ceil(T/g) - 1
+ * cut into blocks of B consecutive groups, B = 256 / ceil(g * G / 32) (the
+ * groups the attention runs at once on one XCD of the MI355X: 256 resident
+ * waves, ceil(g * G / 32) waves per group); blocks in increasing index order,
+ * and within a block the groups by ascending union size (the number of
+ * distinct pages the members select), equal sizes in increasing index.
+ * pw_union_attention_tiled_ordered runs the groups listed last first.
  *
  * In : as pw_group.  Out: query_ids int32 [H_kv][T], identical to pw_group's;
  *      group_order int32 [H_kv][ceil(T/g)] (device).

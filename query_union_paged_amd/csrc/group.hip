@@ -336,10 +336,10 @@ hipError_t launch_group(const pw_shape& s, const int32_t* sel, int W, int g, int
   return launch_c<4, 4>(s, sel, W, g, ids, usize, stream);
 }
 
-// ---- execution order of the groups: per KV head, the groups by ascending
-// union size, equal sizes in index order (a stable counting sort).  One
-// workgroup of 16 waves per KV head; wave w owns a contiguous segment of the
-// head's groups.  The waves count their segments' sizes into per-wave LDS
+// ---- execution order of the groups: per KV head and block of consecutive
+// groups, the block's groups by ascending union size, equal sizes in index
+// order (a stable counting sort).  One workgroup of 16 waves per (KV head,
+// block); wave w owns a contiguous segment of the block's groups.  The waves count their segments' sizes into per-wave LDS
 // histograms; an exclusive scan over (size, wave) turns those into the first
 // output position of every (wave, size); each wave then walks its segment 64
 // groups at a time in index order, the lanes holding equal sizes finding each
@@ -350,14 +350,23 @@ namespace {
 constexpr int kMaxUnion = 1024;          // union sizes are at most N_pages <= 1024
 constexpr int kKeys = kMaxUnion + 1;
 constexpr int kOrderWaves = 16;
+// The attention keeps 256 waves resident per XCD (32 CUs x 8 waves); the groups
+// those waves run at once are the ones whose page sweeps should stay in step, so
+// the order sorts blocks of that many groups (256 / waves per group) and keeps
+// the blocks themselves in index order.
+constexpr int kResidentWavesPerXcd = 256;
 
 __global__ __launch_bounds__(64 * kOrderWaves) void group_order_kernel(
-    const int32_t* __restrict__ usize, int ngroups, int32_t* __restrict__ order) {
+    const int32_t* __restrict__ usize, int ngroups_head, int block, int32_t* __restrict__ order) {
   __shared__ int cnt[kOrderWaves][kKeys];
   __shared__ int wsum[kOrderWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int32_t* sz = usize + (size_t)blockIdx.x * ngroups;
-  int32_t* out = order + (size_t)blockIdx.x * ngroups;
+  // this workgroup's block: `block` consecutive groups of one KV head
+  const int nblk = (ngroups_head + block - 1) / block;
+  const int hh = blockIdx.x / nblk, b0 = (blockIdx.x - hh * nblk) * block;
+  const int ngroups = min(block, ngroups_head - b0);
+  const int32_t* sz = usize + (size_t)hh * ngroups_head + b0;
+  int32_t* out = order + (size_t)hh * ngroups_head + b0;
   const int seg = (ngroups + kOrderWaves - 1) / kOrderWaves;
   const int s0 = min(ngroups, wave * seg), s1 = min(ngroups, s0 + seg);
   auto key_of = [&](int i) __attribute__((always_inline)) {
@@ -427,7 +436,7 @@ __global__ __launch_bounds__(64 * kOrderWaves) void group_order_kernel(
     const int pos = live ? cnt[wave][key] + __popcll(eq & below) : 0;
     wave_sync();
     if (live) {
-      out[pos] = i;
+      out[pos] = b0 + i;
       if ((eq >> lane) == 1ull) cnt[wave][key] += __popcll(eq);   // the highest lane of its size
     }
     wave_sync();
@@ -439,8 +448,11 @@ __global__ __launch_bounds__(64 * kOrderWaves) void group_order_kernel(
 hipError_t launch_group_order(const pw_shape& s, int g, const int32_t* usize, int32_t* order,
                               hipStream_t stream) {
   const int ngroups = (s.T + g - 1) / g;
-  hipLaunchKernelGGL(group_order_kernel, dim3(s.H_kv), dim3(64 * kOrderWaves), 0, stream, usize,
-                     ngroups, order);
+  const int waves_per_group = (g * (s.H_q / s.H_kv) + 31) / 32;
+  const int block = max(1, kResidentWavesPerXcd / waves_per_group);
+  const int nblk = (ngroups + block - 1) / block;
+  hipLaunchKernelGGL(group_order_kernel, dim3(s.H_kv * nblk), dim3(64 * kOrderWaves), 0, stream,
+                     usize, ngroups, block, order);
   return hipGetLastError();
 }
 

@@ -42,7 +42,9 @@ __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
 // usize (optional): the union size of every group, int32 [H_kv][ceil(T / g)]
 hipError_t launch_group(const pw_shape& s, const int32_t* sel, int W, int g, int32_t* ids,
                         hipStream_t stream, int32_t* usize = nullptr);
-// Per KV head, the groups by ascending union size (equal sizes in index order).
+// Per KV head and block of consecutive groups (the groups the attention runs at
+// once on one XCD), the block's groups by ascending union size (equal sizes in
+// index order); blocks stay in index order.
 hipError_t launch_group_order(const pw_shape& s, int g, const int32_t* usize, int32_t* order,
                               hipStream_t stream);
 // FP8 K/V pages re-tiled in MFMA operand order (K tiles, then V tiles), then

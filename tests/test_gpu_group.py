@@ -157,8 +157,9 @@ def _union_sizes(sel_np, ids, N, g):
 
 @pytest.mark.parametrize("case", ["prefill_8k", "rand256", "rand512_ragged", "wide1024"])
 def test_group_order(case):
-    # pw_group_ordered: the same IDs as pw_group, and per KV head the groups by ascending union
-    # size with equal sizes in index order (checked against sizes counted here with numpy)
+    # pw_group_ordered: the same IDs as pw_group, and per KV head and block of groups the block's
+    # groups by ascending union size with equal sizes in index order (checked against sizes
+    # counted here with numpy)
     pw = _pw()
     log(f"[case] pw_group_ordered {case}")
     if case == "prefill_8k":
@@ -171,7 +172,8 @@ def test_group_order(case):
         W, g = {"rand256": (64, 8), "rand512_ragged": (300, 5), "wide1024": (1024, 8)}[case]
         sel = rng.integers(-3, N + 3, size=(2, T, 12)).astype(np.int32)
         sel[:, ::3] %= 24                    # clustered rows: many groups of equal union size
-        Hq = 2
+        # G = 16 makes a group of 8 four waves: blocks of 64 groups (two per head here)
+        Hq = {"rand256": 32, "rand512_ragged": 8, "wide1024": 2}[case]
     H, T, S = sel.shape
     shp = pw.shape(T, Hq, H, 128, P, N, S)
     sel_d = torch.from_numpy(sel).cuda()
@@ -182,7 +184,12 @@ def test_group_order(case):
     ids_np, order_np = ids.cpu().numpy(), order.cpu().numpy()
     sizes = _union_sizes(sel, ids_np, N, g)
     ng = sizes.shape[1]
+    block = max(1, 256 // -(-g * (Hq // H) // 32))         # groups run at once on one XCD
     for h in range(H):
-        want = np.lexsort((np.arange(ng), sizes[h]))       # by size, then by index
-        assert np.array_equal(order_np[h], want), f"head {h}"
-    log(f"[parity] {case}: {ng} groups per head, union sizes {sizes.min()}..{sizes.max()}")
+        want = []
+        for b0 in range(0, ng, block):                      # blocks in index order
+            idx = np.arange(b0, min(ng, b0 + block))
+            want += list(idx[np.lexsort((idx, sizes[h, idx]))])   # by size, then by index
+        assert np.array_equal(order_np[h], np.array(want)), f"head {h}"
+    log(f"[parity] {case}: {ng} groups per head in blocks of {block}, union sizes "
+        f"{sizes.min()}..{sizes.max()}")
