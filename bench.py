@@ -267,8 +267,9 @@ def dense_arms(pw, torch, wl, inp, dev, shp, O, calls, cold_ms, F_u):
 
 
 def ordered_stages(pw, torch, wl, shp, q, k, v, sc, sel, ws, O):
-    """The complete call with each KV head's groups run by ascending union size
-    (pw_group_ordered + pw_tile_kv + pw_union_attention_tiled_ordered)."""
+    """The complete call with each KV head's groups run in the order pw_group_ordered emits
+    (blocks of the groups one XCD runs at once, each by ascending union size):
+    pw_group_ordered + pw_tile_kv + pw_union_attention_tiled_ordered."""
     import ctypes
     ids = torch.empty((wl.H_kv, wl.T), dtype=torch.int32, device="cuda")
     order = torch.empty((wl.H_kv, -(-wl.T // wl.g)), dtype=torch.int32, device="cuda")
@@ -283,8 +284,8 @@ def ordered_stages(pw, torch, wl, shp, q, k, v, sc, sel, ws, O):
 
 def selector_arm(pw, torch, wl, dev, shp, O, ws, ident, cold_ms):
     """The synthetic GPU selector (sink + 2 local pages + top pages by block key sums) and the
-    complete call on its selections, regrouped (the search's group order, and the groups run
-    by ascending union size) and with identity grouping (cold calls)."""
+    complete call on its selections, regrouped (in the search's group order, and in the order
+    pw_group_ordered emits) and with identity grouping (cold calls)."""
     sws = torch.empty(pw.pw_select_workspace_bytes(shp), dtype=torch.uint8, device="cuda")
     sel = torch.empty_like(dev["sel_pages"])
     ids = torch.empty((wl.H_kv, wl.T), dtype=torch.int32, device="cuda")
