@@ -1,8 +1,10 @@
 """Complete-call benchmark of query-union sparse-attention prefill on one MI355X.
 
-One step = one complete call on resident inputs: the grouping search
-(pw_group), the re-tiling of the FP8 pages (pw_tile_kv) and the union attention
-(pw_union_attention_tiled), all on one stream, each bracketed by HIP events.
+One step = one complete call on resident inputs: the grouping search with its
+group order (pw_group_ordered), the re-tiling of the FP8 pages (pw_tile_kv) and
+the union attention in that order (pw_union_attention_tiled_ordered), all on one
+stream, each bracketed by HIP events.  The same call in the search's own group
+order (pw_group + pw_union_attention_tiled, bit-identical output) is an arm.
 Every timed step is cold: a 1 GiB buffer is written before it (outside its
 events), which evicts the MALL and the L2.  Warm steps (no flush) are reported
 beside it.  Default workload: 64K-token prefill of a Llama-3-8B-like layer
@@ -386,7 +388,14 @@ def main():
     def attend(ids_=ids, g=wl.g, sel_=sel):
         return lambda: pw.pw_union_attention_tiled(shp, q, sel_, ids_, g, ws, O=O)
 
-    stages = [search(), tile, attend()]
+    order = torch.empty((wl.H_kv, -(-wl.T // wl.g)), dtype=torch.int32, device="cuda")
+    gws = torch.empty(max(1, pw.pw_group_ordered_workspace_bytes(shp, wl.W, wl.g)),
+                      dtype=torch.uint8, device="cuda")
+    search_ordered = lambda: pw.pw_group_ordered(shp, sel, wl.W, wl.g, query_ids=ids,
+                                                 group_order=order, workspace=gws)
+    attend_ordered = lambda: pw.pw_union_attention_tiled(shp, q, sel, ids, wl.g, ws, O=O,
+                                                         group_order=order)
+    stages = [search_ordered, tile, attend_ordered]
     calls = Calls(torch)
     calls.run(stages, args.warmup, cold=False)           # untimed warm-up
     torch.cuda.synchronize()
@@ -407,7 +416,8 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # roofline of the dominant kernel (union_attn_kernel, launched by pw_union_attention_tiled)
+    # roofline of the dominant kernel (union_attn_kernel, launched by
+    # pw_union_attention_tiled_ordered)
     ids_np = ids.cpu().numpy()
     usz = union_stats(inp["sel_pages"], ids_np, wl.g, wl.N)
     n_pages_total = int(usz.sum())                 # (group, union page) pairs per launch
@@ -422,7 +432,7 @@ def main():
     traffic = recorded_traffic(wl.name)
     roof = {"bound": "mfma", "achieved": achieved, "peak": BF16_MFMA_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": achieved / BF16_MFMA_PEAK_TFLOPS, "traffic": traffic,
-            "kernel": "union_attn_kernel (pw_union_attention_tiled), mean of the timed cold steps",
+            "kernel": "union_attn_kernel (pw_union_attention_tiled_ordered), mean of the timed cold steps",
             "flops_per_unit": 4 * wl.D, "unit_def": "(visible selected key, Q head) pair",
             "units_per_launch": F_u / (4 * wl.D), "kernel_ms": attn_s * 1e3,
             "complete_call": {"achieved": value, "frac": value / BF16_MFMA_PEAK_TFLOPS,
@@ -455,8 +465,8 @@ def main():
             arms[name] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12,
                           "union_pages_mean": float(us.mean()), "union_pages_total": int(us.sum())}
         arms["regroup_gain_vs_identity"] = arms["identity_union8"]["ms"] / ms_per_step
-        ms = cold_ms(ordered_stages(pw, torch, wl, shp, q, k, v, sc, sel, ws, O), n=10)
-        arms["regrouped_size_order"] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12}
+        ms = cold_ms([search(), tile, attend()], n=10)
+        arms["regrouped_search_order"] = {"ms": ms, "useful_TFLOPs": F_u / (ms * 1e-3) / 1e12}
         arms.update(dense_arms(pw, torch, wl, inp, dev, shp, O, calls, cold_ms, F_u))
         arms["selector"] = selector_arm(pw, torch, wl, dev, shp, O, ws, ident, cold_ms)
         arms["head_pipeline"] = head_pipeline_arm(pw, torch, wl, dev, shp, O, ws)
@@ -480,7 +490,8 @@ def main():
         "data": "synthetic (seeded captures, Q/K/V ~ N(0,1), e4m3fn KV with per-page scales)",
         "config": {"workload": wl.name, "tokens": wl.T, "H_q": wl.H_q, "H_kv": wl.H_kv,
                    "head_dim": wl.D, "page": wl.P, "selected_pages": wl.S, "W": wl.W, "g": wl.g,
-                   "kv": "fp8_e4m3fn", "grouping": "regrouped", "timing": "cold (MALL+L2 flushed)"},
+                   "kv": "fp8_e4m3fn", "grouping": "regrouped, group order of pw_group_ordered",
+                   "timing": "cold (MALL+L2 flushed)"},
         "latency_ms": {"complete_call_cold": stats(call_cold), "complete_call_warm": stats(call_warm),
                        "search_cold": stats(cold[:, 0]), "tile_kv_cold": stats(cold[:, 1]),
                        "attention_cold": stats(cold[:, 2]), "search_warm": stats(warm[:, 0]),

@@ -128,6 +128,10 @@ def pw_group(shp: PWShape, sel_pages: torch.Tensor, W: int, g: int,
     return query_ids
 
 
+def pw_group_ordered_workspace_bytes(shp: PWShape, W: int, g: int) -> int:
+    return int(_lib.pw_group_ordered_workspace_bytes(ctypes.byref(shp), W, g))
+
+
 def pw_group_ordered(shp: PWShape, sel_pages: torch.Tensor, W: int, g: int,
                      query_ids: Optional[torch.Tensor] = None,
                      group_order: Optional[torch.Tensor] = None,
