@@ -136,7 +136,8 @@ pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W,
  * In : as pw_group.  Out: query_ids int32 [H_kv][T], identical to pw_group's;
  *      group_order int32 [H_kv][ceil(T/g)] (device).
  * Workspace: pw_group_ordered_workspace_bytes() = H_kv * ceil(T/g) * 4 bytes
- * (the union sizes), required.  Support set and errors as pw_group.
+ * (the union sizes), required; it and group_order must be 4-byte aligned
+ * (else PW_ERR_DIMS).  Support set and other errors as pw_group.
  * ------------------------------------------------------------------------- */
 size_t pw_group_ordered_workspace_bytes(const pw_shape* shape, int32_t W, int32_t g);
 pw_status pw_group_ordered(const pw_shape* shape, const int32_t* sel_pages, int32_t W,

@@ -129,6 +129,8 @@ pw_status pw_group_ordered(const pw_shape* shape, const int32_t* sel_pages, int3
   const size_t need = pw_group_ordered_workspace_bytes(shape, W, g);
   if (!ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
   if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
+  if (((uintptr_t)ws & 3) != 0 || ((uintptr_t)group_order & 3) != 0)
+    return fail(PW_ERR_DIMS, "workspace and group_order must be 4-byte aligned");
   int32_t* usize = static_cast<int32_t*>(ws);
   hipError_t e = pw::launch_group(*shape, sel_pages, W, g, query_ids, (hipStream_t)stream, usize);
   if (e != hipSuccess) return hip_status(e, "pw_group_ordered search launch");

@@ -118,6 +118,8 @@ def test_ordered_validation():
     assert go(ctypes.byref(shp), FAKE, 32, 8, FAKE, None, ws, need, None) == pw.PW_ERR_NULL
     assert go(ctypes.byref(shp), FAKE, 32, 8, FAKE, FAKE, None, need, None) == pw.PW_ERR_NULL
     assert go(ctypes.byref(shp), FAKE, 32, 8, FAKE, FAKE, ws, need - 1, None) == pw.PW_ERR_WORKSPACE
+    assert go(ctypes.byref(shp), FAKE, 32, 8, FAKE, FAKE, ctypes.c_void_p(0x100002), need, None) == pw.PW_ERR_DIMS
+    assert go(ctypes.byref(shp), FAKE, 32, 8, FAKE, ctypes.c_void_p(0x1001), ws, need, None) == pw.PW_ERR_DIMS
     # pw_union_attention_tiled_ordered: the tiled checks plus a required order
     wneed = pw._lib.pw_union_attention_workspace_bytes(ctypes.byref(shp), 8)
     a = pw._lib.pw_union_attention_tiled_ordered
