@@ -136,8 +136,8 @@ def pw_group_ordered(shp: PWShape, sel_pages: torch.Tensor, W: int, g: int,
                      query_ids: Optional[torch.Tensor] = None,
                      group_order: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None, stream=None):
-    """pw_group plus each KV head's groups by ascending union size; returns (query_ids,
-    group_order)."""
+    """pw_group plus an execution order of each KV head's groups (blocks of the groups one XCD
+    runs at once, each block by ascending union size); returns (query_ids, group_order)."""
     sel = _dev(sel_pages, "sel_pages", (torch.int32,), (shp.H_kv, shp.T, shp.S))
     ng = (shp.T + g - 1) // g if g > 0 else 0
     if query_ids is None:
