@@ -291,6 +291,35 @@ pw_status pw_union_attention_tiled_ordered(const pw_shape* shape, const uint16_t
                                            const void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------------
+ * pw_union_attention_tiled_fp8qp -- a lower-precision variant of
+ * pw_union_attention_tiled with Q and P in FP8 as well.
+ *
+ * [abs]: the KV cache is FP8; the pages leave the precision of Q and of the
+ * softmax probabilities open, and the exact path keeps both at bf16 accuracy.
+ * This variant follows the FP8 mode of FlashAttention-3 ([mls-builds]): each Q
+ * row, scaled by a power of two so that its largest magnitude lies in
+ * [128, 256), is rounded to e4m3fn (one part, no residual), and each page's
+ * probabilities p = 2^(s - m) * phi are rounded to e4m3fn, where m is the
+ * row's reference maximum (it moves when a page's largest score passes it by
+ * more than 6, log2 units) and v_scale = phi * 2^k with phi in [1, 2); 2^k is
+ * applied as the MFMA's scale of P.  Both products then run on the FP8 matrix
+ * cores (QK^T at half, PV at about half the matrix cycles of the exact path).
+ * The row sums add the rounded p / phi, so every output row is a convex
+ * combination of its visible V rows.  The result differs from the method's
+ * exact attention by the e4m3 rounding of q and p (measured on the benchmark
+ * workloads: max-abs errors of a few 1e-2 on N(0,1) data); it is NOT within
+ * the tolerance the exact path meets.
+ *
+ * Arguments, layouts, workspace and errors as pw_union_attention_tiled, plus
+ * group_order as pw_union_attention_tiled_ordered, here optional (NULL: the
+ * groups run in index order).  V scales must lie in [2^-127, 2^127].
+ * ------------------------------------------------------------------------- */
+pw_status pw_union_attention_tiled_fp8qp(const pw_shape* shape, const uint16_t* Q,
+                                         const int32_t* sel_pages, const int32_t* query_ids,
+                                         const int32_t* group_order, int32_t g, uint16_t* O,
+                                         const void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
  * pw_union_attention_heads -- pw_union_attention for KV heads
  * [h_begin, h_begin + h_count) only.
  *
@@ -431,7 +460,7 @@ const char* pw_last_error(void);
 /* ABI version of this header, PW_ABI_VERSION. */
 int32_t pw_abi_version(void);
 
-#define PW_ABI_VERSION 3
+#define PW_ABI_VERSION 4
 
 #ifdef __cplusplus
 }

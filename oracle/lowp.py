@@ -37,7 +37,8 @@ average of v_scale * V_codes up to the e4m3 rounding of q and p.
 from __future__ import annotations
 
 import math
-from typing import Sequence
+import os
+from typing import Optional, Sequence
 
 import numpy as np
 
@@ -89,38 +90,51 @@ def split_scale(v_scale: float):
     return 2.0 * f, x - 1
 
 
-def attention_query_lowp(pb: Problem, h: int, t: int, tau: float = TAU) -> np.ndarray:
-    """O[t][h*G:(h+1)*G] of the low-precision variant as fp64 [G][D]."""
+def _codes(pb: Problem, h: int):
+    """Decoded K and V codes of KV head h, [N][P][D] each (cached on the problem)."""
+    cache = pb.__dict__.setdefault("_lowp_codes", {})
+    if h not in cache:
+        cache[h] = (decode_e4m3fn(pb.k_codes[:, h]), decode_e4m3fn(pb.v_codes[:, h]))
+    return cache[h]
+
+
+def attention_query_lowp(pb: Problem, h: int, t: int, tau: float = TAU,
+                         trace: Optional[list] = None) -> np.ndarray:
+    """O[t][h*G:(h+1)*G] of the low-precision variant as fp64 [G][D] (the G rows of the
+    query side by side; each keeps its own reference maximum).  With a list as `trace`,
+    every page appends its intermediate values: u, nk (visible keys), the reference m
+    before and after the page (m_in, m), the page maxima mx and the scores s, the
+    unrounded x = 2^(s - m) phi and the rounded p, phi and k."""
     out = np.zeros((pb.G, pb.D))
     sup = pb.support(h, t)                  # ascending, each page once
-    qq = pb.q_rows(t, h)
-    kc = decode_e4m3fn(pb.k_codes[:, h])    # [N][P][D] codes
-    vc = decode_e4m3fn(pb.v_codes[:, h])
+    sup = sup[sup * pb.P <= t]              # pages with at least one visible key
+    if sup.size == 0:
+        return out
+    kc, vc = _codes(pb, h)
+    qt = np.stack([quantize_q_row(q) for q in pb.q_rows(t, h)])     # [G][D]
     c = math.log2(math.e) / math.sqrt(pb.D)
-    for r in range(pb.G):
-        qt = quantize_q_row(qq[r])
-        m = -math.inf
-        num = np.zeros(pb.D)
-        den = 0.0
-        for u in sup:
-            u = int(u)
-            keys = [j for j in range(pb.P) if u * pb.P + j <= t]
-            if not keys:
-                continue
-            s = (kc[u, keys] @ qt) * pb.scales[0, u, h] * c
-            mx = float(s.max())
-            if mx > m + tau:                # the reference moves (step 3)
-                if m > -math.inf:
-                    num *= 2.0 ** (m - mx)
-                    den *= 2.0 ** (m - mx)
-                m = mx
-            phi, k = split_scale(float(pb.scales[1, u, h]))
-            p = e4m3_rne(np.exp2(s - m) * phi)
-            num += 2.0 ** k * (p @ vc[u, keys])
-            den += float(p.sum()) / phi
-        if den > 0.0:
-            out[r] = num / den
-    return out
+    m = np.full(pb.G, -np.inf)
+    num = np.zeros((pb.G, pb.D))
+    den = np.zeros(pb.G)
+    for u in sup:
+        u = int(u)
+        nk = min(pb.P, t - u * pb.P + 1)    # visible keys 0 .. nk - 1
+        s = (qt @ kc[u, :nk].T) * pb.scales[0, u, h] * c           # [G][nk]
+        mx = s.max(axis=1)
+        move = mx > m + tau                 # the reference moves (step 3)
+        f = np.where(move & (m > -np.inf), np.exp2(np.where(move, m - mx, 0.0)), 1.0)
+        num *= f[:, None]
+        den *= f
+        m_in, m = m, np.where(move, mx, m)
+        phi, k = split_scale(float(pb.scales[1, u, h]))
+        x = np.exp2(s - m[:, None]) * phi
+        p = e4m3_rne(x)
+        num += 2.0 ** k * (p @ vc[u, :nk])
+        den += p.sum(axis=1) / phi
+        if trace is not None:
+            trace.append({"u": u, "nk": nk, "m_in": m_in, "m": m, "mx": mx, "s": s, "x": x,
+                          "p": p, "phi": phi, "k": k})
+    return num / den[:, None]
 
 
 def attention_pairs_lowp(pb: Problem, pairs: Sequence[tuple], tau: float = TAU) -> np.ndarray:
@@ -128,4 +142,45 @@ def attention_pairs_lowp(pb: Problem, pairs: Sequence[tuple], tau: float = TAU) 
     out = np.empty((len(pairs), pb.G, pb.D))
     for i, (h, t) in enumerate(pairs):
         out[i] = attention_query_lowp(pb, int(h), int(t), tau)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Process-pool driver (fork; the decoded Problem is shared copy-on-write).
+
+_POOL_PB: Optional[Problem] = None
+
+
+def _work(chunk):
+    from threadpoolctl import threadpool_limits
+    with threadpool_limits(limits=1):
+        return attention_pairs_lowp(_POOL_PB, chunk)
+
+
+def attention_pairs_lowp_parallel(pb: Problem, pairs: Sequence[tuple],
+                                  workers: Optional[int] = None) -> np.ndarray:
+    """Same as ``attention_pairs_lowp`` spread over host cores (one process each)."""
+    global _POOL_PB
+    workers = workers or len(os.sched_getaffinity(0))
+    pairs = [(int(h), int(t)) for h, t in pairs]
+    if workers <= 1 or len(pairs) < 64:
+        return attention_pairs_lowp(pb, pairs)
+    for h in sorted({h for h, _ in pairs}):      # decode before fork
+        _codes(pb, h)
+    import multiprocessing as mp
+    n_chunks = workers * 4
+    chunks = [c for c in (pairs[i::n_chunks] for i in range(n_chunks)) if c]
+    _POOL_PB = pb
+    try:
+        pool = mp.get_context("fork").Pool(workers)
+        try:
+            parts = pool.map(_work, chunks)
+        finally:
+            pool.close()
+            pool.join()
+    finally:
+        _POOL_PB = None
+    out = np.empty((len(pairs), pb.G, pb.D))
+    for i, part in enumerate(parts):
+        out[i::len(chunks)] = part
     return out

@@ -247,7 +247,8 @@ pw_status pw_tile_kv(const pw_shape* shape, const uint8_t* K_fp8, const uint8_t*
 static pw_status tiled_attention(const pw_shape* shape, const uint16_t* Q,
                                  const int32_t* sel_pages, const int32_t* query_ids,
                                  const int32_t* group_order, int32_t g, uint16_t* O,
-                                 const void* ws, size_t ws_bytes, void* stream, const char* what) {
+                                 const void* ws, size_t ws_bytes, void* stream, const char* what,
+                                 bool fp8_qp = false) {
   pw_status st = check_shape(shape);
   if (st != PW_OK) return st;
   if (!Q || !sel_pages || !query_ids || !O)
@@ -258,7 +259,7 @@ static pw_status tiled_attention(const pw_shape* shape, const uint16_t* Q,
   if (st != PW_OK) return st;
   return hip_status(pw::launch_union_attention_tiled(*shape, Q, sel_pages, query_ids, g, 0,
                                                      shape->H_kv, O, ws, (hipStream_t)stream,
-                                                     group_order),
+                                                     group_order, fp8_qp),
                     what);
 }
 
@@ -276,6 +277,14 @@ pw_status pw_union_attention_tiled_ordered(const pw_shape* shape, const uint16_t
   if (!group_order) return fail(PW_ERR_NULL, "group_order is required");
   return tiled_attention(shape, Q, sel_pages, query_ids, group_order, g, O, ws, ws_bytes, stream,
                          "pw_union_attention_tiled_ordered launch");
+}
+
+pw_status pw_union_attention_tiled_fp8qp(const pw_shape* shape, const uint16_t* Q,
+                                         const int32_t* sel_pages, const int32_t* query_ids,
+                                         const int32_t* group_order, int32_t g, uint16_t* O,
+                                         const void* ws, size_t ws_bytes, void* stream) {
+  return tiled_attention(shape, Q, sel_pages, query_ids, group_order, g, O, ws, ws_bytes, stream,
+                         "pw_union_attention_tiled_fp8qp launch", true);
 }
 
 size_t pw_dense_union_ref_workspace_bytes(const pw_shape* shape) {

@@ -18,6 +18,9 @@ constexpr float kTau = 24.0f;
 // squares, of the square roots and of the score accumulation, and the residual
 // of the two-part e4m3 split of Q (below 1e-4 of a row's norm).
 constexpr float kNormSlack = 1.0f + 1.0f / 512;
+// The FP8 Q and P variant rounds p to e4m3fn (largest value 448): its threshold
+// keeps p <= 2^kTauFp8 * phi < 2^7 with the V scale's mantissa phi in [1, 2).
+constexpr float kTauFp8 = 6.0f;
 
 
 // Physical key held by MFMA row i of key tile kt.  Output register r of a lane
@@ -63,13 +66,15 @@ __device__ __forceinline__ uint4 load16(const uint8_t* p) {
 // is the scaled bf16 value for elements >= 2^-2 and within 2^-10 below, so
 // K^T runs on the FP8 MFMA straight from the cache bytes; rscale = 2^-e is
 // folded back into the score scale.  qn bounds the norm of the scaled row.
+// Without SPLIT (the FP8 Q and P variant) the row is hi alone, and qn bounds
+// the norm of hi.
 template <int D>
 struct QRow {
   i32x8 hi[D / 64], lo[D / 64];
   float rscale, qn;
 };
 
-template <int D>
+template <int D, bool SPLIT = true>
 __device__ __forceinline__ void load_q_row(const uint16_t* qp, bool ok, QRow<D>& r) {
   constexpr int KQ = D / 64;
   float q[D / 2];
@@ -102,15 +107,20 @@ __device__ __forceinline__ void load_q_row(const uint16_t* qp, bool ok, QRow<D>&
       const float* x = q + 32 * ks + 4 * w;
       const float x0 = ldexpf(x[0], e), x1 = ldexpf(x[1], e);
       const float x2 = ldexpf(x[2], e), x3 = ldexpf(x[3], e);
-      ssq = fmaf(x0, x0, fmaf(x1, x1, fmaf(x2, x2, fmaf(x3, x3, ssq))));
+      if constexpr (SPLIT) ssq = fmaf(x0, x0, fmaf(x1, x1, fmaf(x2, x2, fmaf(x3, x3, ssq))));
       int hi = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
       hi = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, hi, true);
       const auto h01 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
       const auto h23 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
-      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01[0], x1 - h01[1], 0, false);
-      lo = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23[0], x3 - h23[1], lo, true);
-      r.hi[ks][w] = hi;
-      r.lo[ks][w] = lo;
+      if constexpr (SPLIT) {
+        int lo = __builtin_amdgcn_cvt_pk_fp8_f32(x0 - h01[0], x1 - h01[1], 0, false);
+        lo = __builtin_amdgcn_cvt_pk_fp8_f32(x2 - h23[0], x3 - h23[1], lo, true);
+        r.hi[ks][w] = hi;
+        r.lo[ks][w] = lo;
+      } else {
+        ssq = fmaf(h01[0], h01[0], fmaf(h01[1], h01[1], fmaf(h23[0], h23[0], fmaf(h23[1], h23[1], ssq))));
+        r.hi[ks][w] = hi;
+      }
     }
   }
   r.qn = sqrtf(ssq + __shfl_xor(ssq, 32)) * kNormSlack;
@@ -119,7 +129,8 @@ __device__ __forceinline__ void load_q_row(const uint16_t* qp, bool ok, QRow<D>&
 // ---- S^T = K (Qhi + Qlo)^T on the FP8 MFMA, one page of 64 key slots ------
 // kr[kt][c]: the lane's 16-byte K chunks of key tile kt (tiled page order).
 // Key tiles innermost, so consecutive MFMAs accumulate into different tiles.
-template <int D>
+// PARTS = 1: K Qhi^T only (the FP8 Q and P variant).
+template <int D, int PARTS = 2>
 __device__ __forceinline__ void qk_page(const uint4 (&kr)[2][D / 32], const QRow<D>& q,
                                         f32x16 (&sc)[2]) {
 #pragma unroll
@@ -129,7 +140,7 @@ __device__ __forceinline__ void qk_page(const uint4 (&kr)[2][D / 32], const QRow
 #pragma unroll
   for (int ks = 0; ks < D / 64; ++ks) {
 #pragma unroll
-    for (int part = 0; part < 2; ++part) {
+    for (int part = 0; part < PARTS; ++part) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
         const uint4 w0 = kr[kt][2 * ks], w1 = kr[kt][2 * ks + 1];
@@ -212,6 +223,55 @@ __device__ __forceinline__ float softmax_page(f32x16 (&sc)[2], bool member, cons
   return alpha;
 }
 
+// ---- the same page for the FP8 Q and P variant ----------------------------
+// The threshold is kTauFp8, and the V scale is split as v_scale = phi 2^vk with
+// vk = floor(log2 v_scale): phi folds into the exponent (p = 2^(s - m) phi <=
+// 2^7), 2^vk becomes the E8M0 scale *vsb of the P operand of the PV MFMA.  The
+// probabilities are rounded to e4m3fn (round to nearest even) into pF, byte i
+// of a lane being key 32 hf + i, and the row sums add those rounded values
+// (converted back exactly) times 1 / phi, so the weights of a row sum to one.
+__device__ __forceinline__ float softmax_page_fp8(f32x16 (&sc)[2], bool member, const float4 f,
+                                                  float rscale, float qn, float& m_run,
+                                                  float& l_run, i32x8& pF, int& vsb) {
+  const float ksc = f.x * rscale;
+  const float lim = m_run + kTauFp8;
+  const bool may_move = member && !(qn * f.y * rscale <= lim);
+  float m_new = m_run, alpha = 1.f;
+  if (__ballot(may_move)) {
+    float mx = max_raw(sc[0][0], sc[0][1]);
+#pragma unroll
+    for (int i = 2; i < 32; i += 2) mx = max3_raw(mx, sc[i >> 4][i & 15], sc[i >> 4][(i & 15) + 1]);
+    mx = half_max(mx);
+    const float mx2 = mx * ksc;
+    m_new = (member && mx2 > lim) ? mx2 : m_run;
+    alpha = __builtin_amdgcn_exp2f((m_new == m_run) ? 0.f : m_run - m_new);
+  }
+  m_run = m_new;
+  const float vk = floorf(f.z);
+  vsb = min(max(127 + (int)vk, 0), 254);
+  const float bias = (member && m_new > -INFINITY) ? ((f.z - vk) - m_new) : -INFINITY;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+  float ps = 0.f;
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const f32x16& t = sc[w >> 2];
+    const int r = 4 * (w & 3);
+    const float e0 = __builtin_amdgcn_exp2f(fmaf(t[r], ksc, bias));
+    const float e1 = __builtin_amdgcn_exp2f(fmaf(t[r + 1], ksc, bias));
+    const float e2 = __builtin_amdgcn_exp2f(fmaf(t[r + 2], ksc, bias));
+    const float e3 = __builtin_amdgcn_exp2f(fmaf(t[r + 3], ksc, bias));
+    int x = __builtin_amdgcn_cvt_pk_fp8_f32(e0, e1, 0, false);
+    x = __builtin_amdgcn_cvt_pk_fp8_f32(e2, e3, x, true);
+    pF[w] = x;
+    ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, false),
+                                         ones, ps, false);
+    ps = __builtin_amdgcn_fdot2_f32_bf16(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x, 1.0f, true),
+                                         ones, ps, false);
+  }
+  l_run = fmaf(ps, ldexpf(f.w, (int)vk), l_run * alpha);
+  return alpha;
+}
+
 template <int D>
 __device__ __forceinline__ void rescale_acc(f32x16 (&acc)[D / 32], float alpha) {
   if (__ballot(alpha != 1.f)) {
@@ -236,6 +296,22 @@ __device__ __forceinline__ void pv_page(const uint4 (&vr)[D / 32][2], const bf16
       const bf16x8 a = (q & 1) ? fp8x8_to_bf16(w.z, w.w) : fp8x8_to_bf16(w.x, w.y);
       acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pB[q], acc[dt], 0, 0, 0);
     }
+  }
+}
+
+// ---- O^T += V^T P^T on the FP8 MFMA (the FP8 Q and P variant): one MFMA per
+// d tile over all 64 keys; A = the lane's 32 V codes of one d (keys 32 hf ..
+// 32 hf + 31), B = the lane's 32 e4m3 probabilities of the same keys, scaled
+// by 2^(vsb - 127).
+template <int D>
+__device__ __forceinline__ void pv_page_fp8(const uint4 (&vr)[D / 32][2], const i32x8& pF, int vsb,
+                                            f32x16 (&acc)[D / 32]) {
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const uint4 w0 = vr[dt][0], w1 = vr[dt][1];
+    const i32x8 a = {(int)w0.x, (int)w0.y, (int)w0.z, (int)w0.w,
+                     (int)w1.x, (int)w1.y, (int)w1.z, (int)w1.w};
+    acc[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, pF, acc[dt], 0, 0, 0, 127, 0, vsb);
   }
 }
 

@@ -61,10 +61,11 @@ hipError_t launch_union_attention(const pw_shape& s, const uint16_t* Q, const ui
 // h_begin .. h_begin + h_count - 1.
 // order (optional): per KV head, the execution order of its groups (a
 // permutation of 0 .. ceil(T / g) - 1, the last entries run first).
+// fp8_qp: the lower-precision variant with Q and P rounded to e4m3fn.
 hipError_t launch_union_attention_tiled(const pw_shape& s, const uint16_t* Q, const int32_t* sel,
                                         const int32_t* ids, int g, int h_begin, int h_count,
                                         uint16_t* O, const void* ws, hipStream_t stream,
-                                        const int32_t* order = nullptr);
+                                        const int32_t* order = nullptr, bool fp8_qp = false);
 hipError_t launch_pair_attention(const pw_shape& s, const uint16_t* Q, const uint8_t* tiles,
                                  const float* scales, const int2* plist, const int* pcount,
                                  const int* tstart, const int2* pairs, int tiles_head,

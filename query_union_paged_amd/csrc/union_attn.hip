@@ -76,7 +76,7 @@ struct UAParams {
   int Np, Tc, t0, tiles_head;
 };
 
-enum : int { kUnionMode = 0, kPairMode = 1 };
+enum : int { kUnionMode = 0, kPairMode = 1, kFp8Mode = 2 };
 
 // Re-tiles the FP8 pages of one layer into MFMA operand order (one workgroup
 // per (page, KV head) block of 64 key slots x D bytes, for K and for V; both
@@ -182,6 +182,8 @@ __global__ __launch_bounds__(256) void tile_kv_kernel(const uint8_t* __restrict_
 // MODE kUnionMode: groups of query IDs, union of their selected pages, O out.
 // MODE kPairMode: up to 8 entries of one page pair's membership list, the pair's
 // pages they selected, unnormalised partials out (direct KV-page union).
+// MODE kFp8Mode: as kUnionMode with Q and P rounded to e4m3fn per row, QK^T on
+// K Qhi^T alone and PV on the FP8 MFMA (a lower-precision variant).
 template <int D, int P, int MODE>
 __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAParams p) {
   // P in {16, 32, 64} keys per page; the tiled pages always hold 64 key slots
@@ -217,7 +219,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   int h, gm, n_u = 0;
   int my_t = -1, my_slot = -1;              // lane i < gm: member i's token (and slot)
 
-  if constexpr (MODE == kUnionMode) {
+  if constexpr (MODE != kPairMode) {
   const int hl = gid / p.groups_per_head;
   h = p.h_begin + hl;
   int k = gid - hl * p.groups_per_head;
@@ -338,7 +340,8 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   const int pslot = __shfl(my_slot, s_ & 63);
   const int qhead = h * p.G + (n - s_ * p.G);
   QRow<D> qr;
-  load_q_row<D>(p.Q + ((size_t)(ok ? t_ : 0) * p.Hq + qhead) * D + (D / 2) * hf, ok, qr);
+  load_q_row<D, MODE != kFp8Mode>(p.Q + ((size_t)(ok ? t_ : 0) * p.Hq + qhead) * D + (D / 2) * hf,
+                                  ok, qr);
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x16 acc[DT];
@@ -396,18 +399,27 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
     pfr = pfac[(size_t)u0 * p.Hkv];
   }
   bf16x8 pB[4];
+  i32x8 pF;
+  int vsb = 127;
   for (int up = 0; up < n_u; ++up) {
     const uint32_t ent = __builtin_amdgcn_readfirstlane(list[up]);
     const float4 pf_c = pfr;
     const int u1 = page_of(up + 1);
-    qk_page<D>(kbuf, qr, sacc);
+    qk_page<D, MODE == kFp8Mode ? 1 : 2>(kbuf, qr, sacc);
     load_k(kbuf, u1);                     // K registers are free once the MFMAs have read them
     pfr = pfac[(size_t)u1 * p.Hkv];
     mask_page<P>(sacc, ent & 0xFFFF, tmin, trow, hf);
     const bool member = slot >= 0 && (((ent >> 16) >> slot) & 1u);
-    const float alpha = softmax_page(sacc, member, pf_c, qr.rscale, qr.qn, m_run, l_run, pB);
-    rescale_acc<D>(acc, alpha);
-    pv_page<D>(vbuf, pB, acc);
+    if constexpr (MODE == kFp8Mode) {
+      const float alpha =
+          softmax_page_fp8(sacc, member, pf_c, qr.rscale, qr.qn, m_run, l_run, pF, vsb);
+      rescale_acc<D>(acc, alpha);
+      pv_page_fp8<D>(vbuf, pF, vsb, acc);
+    } else {
+      const float alpha = softmax_page(sacc, member, pf_c, qr.rscale, qr.qn, m_run, l_run, pB);
+      rescale_acc<D>(acc, alpha);
+      pv_page<D>(vbuf, pB, acc);
+    }
     load_v(vbuf, u1);
   }
 
@@ -479,7 +491,7 @@ hipError_t tile_kv(const pw_shape& s, const uint8_t* K, const uint8_t* V, const 
 hipError_t launch_union_attention_tiled(const pw_shape& s, const uint16_t* Q, const int32_t* sel,
                                         const int32_t* ids, int g, int h_begin, int h_count,
                                         uint16_t* O, const void* ws, hipStream_t stream,
-                                        const int32_t* order) {
+                                        const int32_t* order, bool fp8_qp) {
   const uint8_t* tiles = static_cast<const uint8_t*>(ws);
   UAParams prm;
   common_params(prm, s, Q, nullptr);
@@ -498,6 +510,9 @@ hipError_t launch_union_attention_tiled(const pw_shape& s, const uint16_t* Q, co
   prm.total_items = prm.total_groups * prm.n_rt;
   const int blocks = (prm.total_items + PW_UA_WG_WAVES - 1) / PW_UA_WG_WAVES;
   const size_t lds = (size_t)prm.lds_wave * PW_UA_WG_WAVES;
+  if (fp8_qp)
+    return s.D == 128 ? launch_d<128, kFp8Mode>(prm, blocks, lds, stream)
+                      : launch_d<64, kFp8Mode>(prm, blocks, lds, stream);
   return s.D == 128 ? launch_d<128, kUnionMode>(prm, blocks, lds, stream)
                     : launch_d<64, kUnionMode>(prm, blocks, lds, stream);
 }

@@ -57,6 +57,8 @@ _SIGS = {
     "pw_union_attention_tiled": (_i32, [_SHP, _vp, _vp, _vp, _i32, _vp, _vp, _sz, _vp]),
     "pw_union_attention_tiled_ordered": (_i32, [_SHP, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz,
                                                 _vp]),
+    "pw_union_attention_tiled_fp8qp": (_i32, [_SHP, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _sz,
+                                              _vp]),
     "pw_check_ids_workspace_bytes": (_sz, [_SHP]),
     "pw_check_ids": (_i32, [_SHP, _vp, _vp, _vp, _sz, _vp]),
     "pw_select_workspace_bytes": (_sz, [_SHP]),
@@ -252,6 +254,28 @@ def pw_union_attention_tiled(shp: PWShape, Q, sel_pages, query_ids, g: int,
         _check(_lib.pw_union_attention_tiled_ordered(ctypes.byref(shp), q, sel, ids, order, g, o,
                                                      ws, workspace.numel(), _stream(stream)),
                "pw_union_attention_tiled_ordered")
+    return O
+
+
+def pw_union_attention_tiled_fp8qp(shp: PWShape, Q, sel_pages, query_ids, g: int,
+                                   workspace: torch.Tensor, O: Optional[torch.Tensor] = None,
+                                   stream=None,
+                                   group_order: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The lower-precision variant of pw_union_attention_tiled: Q and P rounded to e4m3fn per
+    row, both products on the FP8 matrix cores (not within the exact path's tolerance)."""
+    T, Hq, Hkv, D, S = shp.T, shp.H_q, shp.H_kv, shp.D, shp.S
+    q = _dev(Q, "Q", _BF16, (T, Hq, D))
+    sel = _dev(sel_pages, "sel_pages", (torch.int32,), (Hkv, T, S))
+    ids = _dev(query_ids, "query_ids", (torch.int32,), (Hkv, T))
+    if O is None:
+        O = torch.empty((T, Hq, D), dtype=torch.bfloat16, device=Q.device)
+    o = _dev(O, "O", _BF16, (T, Hq, D))
+    ws = _dev(workspace, "workspace", (torch.uint8,))
+    order = (None if group_order is None else
+             _dev(group_order, "group_order", (torch.int32,), (Hkv, (T + g - 1) // g)))
+    _check(_lib.pw_union_attention_tiled_fp8qp(ctypes.byref(shp), q, sel, ids, order, g, o, ws,
+                                               workspace.numel(), _stream(stream)),
+           "pw_union_attention_tiled_fp8qp")
     return O
 
 

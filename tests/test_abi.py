@@ -20,7 +20,7 @@ def test_every_declared_symbol_is_exported():
     exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
     missing = [n for n in names if n not in exported]
     assert not missing, missing
-    assert pw._lib.pw_abi_version() == 3
+    assert pw._lib.pw_abi_version() == 4
 
 
 def test_status_strings():
