@@ -45,7 +45,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill_64k")
     ap.add_argument("--no-arms", action="store_true", help="skip the identity / g=1 comparison arms")
-    ap.add_argument("--only-arm", choices=["selector", "dense"], default=None,
+    ap.add_argument("--only-arm", choices=["selector", "dense", "fp8qp"], default=None,
                     help="run only this comparison arm (for profiling it)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU oracle sample time")
@@ -317,6 +317,32 @@ def selector_arm(pw, torch, wl, dev, shp, O, ws, ident, cold_ms):
             "identity_union_pages_mean": float(ui.mean()), "n_local": 2}
 
 
+def fp8qp_arm(pw, torch, wl, shp, q, k, v, sc, sel, ws, calls, F_u, O_exact, n: int = 10):
+    """The complete call with the lower-precision attention (Q and P in e4m3fn,
+    pw_union_attention_tiled_fp8qp) in the order pw_group_ordered emits, cold, and how far its
+    output lies from the exact path's output on the same inputs."""
+    import ctypes
+    ids = torch.empty((wl.H_kv, wl.T), dtype=torch.int32, device="cuda")
+    order = torch.empty((wl.H_kv, -(-wl.T // wl.g)), dtype=torch.int32, device="cuda")
+    gws = torch.empty(max(1, int(pw._lib.pw_group_ordered_workspace_bytes(
+        ctypes.byref(shp), wl.W, wl.g))), dtype=torch.uint8, device="cuda")
+    O8 = torch.empty_like(O_exact)
+    stages = [lambda: pw.pw_group_ordered(shp, sel, wl.W, wl.g, query_ids=ids, group_order=order,
+                                          workspace=gws),
+              lambda: pw.pw_tile_kv(shp, k, v, sc, workspace=ws),
+              lambda: pw.pw_union_attention_tiled_fp8qp(shp, q, sel, ids, wl.g, ws, O=O8,
+                                                        group_order=order)]
+    calls.run(stages, 1, cold=False)
+    t = calls.run(stages, n, cold=True)
+    call_ms = float(np.median(t.sum(axis=1)))
+    kern_ms = float(t[:, 2].mean())
+    d = (O8.float() - O_exact.float()).abs()
+    log(f"[bench] fp8 Q and P: call {call_ms:.3f} ms, attention {kern_ms:.3f} ms")
+    return {"ms": call_ms, "useful_TFLOPs": F_u / (call_ms * 1e-3) / 1e12,
+            "attention_ms": kern_ms, "attention_frac": F_u / (kern_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFLOPS,
+            "vs_exact_path_output": {"max_abs": float(d.max()), "mean_abs": float(d.mean())}}
+
+
 def cpu_model() -> str:
     try:
         for line in open("/proc/cpuinfo"):
@@ -458,6 +484,8 @@ def main():
         arms["selector"] = selector_arm(pw, torch, wl, dev, shp, O, ws, ident, cold_ms)
     elif args.only_arm == "dense":
         arms.update(dense_arms(pw, torch, wl, inp, dev, shp, O, calls, cold_ms, F_u))
+    elif args.only_arm == "fp8qp":
+        arms["fp8qp"] = fp8qp_arm(pw, torch, wl, shp, q, k, v, sc, sel, ws, calls, F_u, O)
     elif not args.no_arms:
         for name, g_arm in [("identity_union8", wl.g), ("per_query_g1", 1)]:
             ms = cold_ms([tile, attend(ident, g_arm)], n=5 if g_arm == 1 else 10)
@@ -470,6 +498,8 @@ def main():
         arms.update(dense_arms(pw, torch, wl, inp, dev, shp, O, calls, cold_ms, F_u))
         arms["selector"] = selector_arm(pw, torch, wl, dev, shp, O, ws, ident, cold_ms)
         arms["head_pipeline"] = head_pipeline_arm(pw, torch, wl, dev, shp, O, ws)
+        stages[-1]()                     # O = the exact path's output again
+        arms["fp8qp"] = fp8qp_arm(pw, torch, wl, shp, q, k, v, sc, sel, ws, calls, F_u, O)
 
     swp = sweep(pw, torch, wl, inp, dev, shp, O, ws) if args.sweep else None
 
