@@ -63,8 +63,9 @@ def parse():
 def union_stats(sel: np.ndarray, ids: np.ndarray, g: int, N: int):
     """Per-group union sizes (pages) from the selections and the query IDs (host, numpy)."""
     H, T, S = sel.shape
-    ng = (T + g - 1) // g
-    pad = ng * g - T
+    Ti = ids.shape[1]                    # ID entries per head (T, or a subset of each group)
+    ng = (Ti + g - 1) // g
+    pad = ng * g - Ti
     idp = np.concatenate([ids, np.full((H, pad), -1, ids.dtype)], axis=1) if pad else ids
     rows = np.where(idp[..., None] >= 0, np.take_along_axis(sel, np.clip(idp, 0, T - 1)[..., None], axis=1), -1)
     rows = rows.reshape(H, ng, g * S)
@@ -73,6 +74,28 @@ def union_stats(sel: np.ndarray, ids: np.ndarray, g: int, N: int):
     distinct = s >= 0
     distinct[:, :, 1:] &= s[:, :, 1:] != s[:, :, :-1]
     return distinct.sum(axis=2)          # [H][ng]
+
+
+def tile_units(sel: np.ndarray, ids: np.ndarray, g: int, G: int, N: int) -> int:
+    """(32-row tile, page) units the attention computes: a group of g * G rows is cut into
+    tiles of 32 rows (slot * G + head), and each tile walks the union of the pages its own
+    slots selected."""
+    n_rt = (g * G + 31) // 32
+    if n_rt == 1:
+        return int(union_stats(sel, ids, g, N).sum())
+    H, T, S = sel.shape
+    ng = (T + g - 1) // g
+    pad = ng * g - T
+    idp = np.concatenate([ids, np.full((H, pad), -1, ids.dtype)], axis=1) if pad else ids
+    idp = idp.reshape(H, ng, g)
+    total = 0
+    for rt in range(n_rt):
+        s_lo, s_hi = (32 * rt) // G, min(g - 1, (32 * rt + 31) // G)
+        if s_lo > s_hi:
+            continue
+        sub = idp[:, :, s_lo:s_hi + 1].reshape(H, -1)
+        total += int(union_stats(sel, sub, s_hi - s_lo + 1, N).sum())
+    return total
 
 
 def pair_entries(sel: np.ndarray, pairs, N: int) -> float:
@@ -446,9 +469,9 @@ def main():
     # pw_union_attention_tiled_ordered)
     ids_np = ids.cpu().numpy()
     usz = union_stats(inp["sel_pages"], ids_np, wl.g, wl.N)
-    n_pages_total = int(usz.sum())                 # (group, union page) pairs per launch
+    n_pages_total = tile_units(inp["sel_pages"], ids_np, wl.g, wl.G, wl.N)   # (tile, page) units
     rows = wl.g * wl.G
-    comp_unit = 4 * ((rows + 31) // 32 * 32) * wl.P * wl.D   # MFMA flops per (group, page)
+    comp_unit = 4 * 32 * wl.P * wl.D                # MFMA flops per (32-row tile, page)
     comp_flops = n_pages_total * comp_unit
     attn_s = float(cold[:, 2].mean()) * 1e-3
     achieved = F_u / attn_s / 1e12
@@ -463,8 +486,8 @@ def main():
             "units_per_launch": F_u / (4 * wl.D), "kernel_ms": attn_s * 1e3,
             "complete_call": {"achieved": value, "frac": value / BF16_MFMA_PEAK_TFLOPS,
                               "ms": ms_per_step},
-            "computed_work": {"flops": comp_flops, "per_group_page": comp_unit,
-                              "group_pages": n_pages_total,
+            "computed_work": {"flops": comp_flops, "per_tile_page": comp_unit,
+                              "tile_pages": n_pages_total,
                               "achieved": comp_flops / attn_s / 1e12,
                               "frac": comp_flops / attn_s / 1e12 / BF16_MFMA_PEAK_TFLOPS,
                               "useful_over_computed": F_u / comp_flops},

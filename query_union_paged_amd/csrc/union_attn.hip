@@ -27,9 +27,9 @@
 //                          to bf16 exactly; d is the MFMA row.
 // Page loads are contiguous 1 KB wave reads of the tiled copy straight into
 // operand registers.  A group of at most 32 rows (G = 4, g = 8) is one wave,
-// which loads each union page once; a 64-row group (G = 8) is two waves, and
-// each of them loads every union page (the page's K/V bytes cross the vector
-// memory path twice per group).  The per-page scales are folded into the
+// which loads each union page once; a 64-row group (G = 8) is two waves, each
+// walking the union of its own four members' pages (pages selected in both
+// halves cross the vector memory path twice per group).  The per-page scales are folded into the
 // scores (k) and into the exponent (v).  The key order inside the 32-row K
 // tiles is permuted so that the PV operands of every lane are 32 consecutive
 // keys of one d in the tiled V copy.
@@ -218,6 +218,10 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   uint32_t* list = reinterpret_cast<uint32_t*>(wbase);        // page | members << 16
   int h, gm, n_u = 0;
   int my_t = -1, my_slot = -1;              // lane i < gm: member i's token (and slot)
+  // The slots (members) whose rows this wave holds: rows 32 rt .. 32 rt + 31 are slot * G +
+  // head.  A page that none of them selected leaves every row of the wave as it is (p = 0,
+  // alpha = 1), so with two row tiles per group each wave walks only its own slots' pages.
+  const int s_lo = (32 * rt) / p.G, s_hi = (32 * rt + 31) / p.G;       // inclusive
 
   if constexpr (MODE != kPairMode) {
   const int hl = gid / p.groups_per_head;
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
       const int t = __shfl(my_t, i & 63);
       pg[it] = -1;
       if (e < n_ent && t >= 0) pg[it] = p.sel[((size_t)h * p.T + t) * p.S + (e - i * p.S)];
-      pg[it] = (pg[it] >= 0 && pg[it] < p.N) ? (pg[it] | (i << 16)) : -1;
+      pg[it] = (pg[it] >= 0 && pg[it] < p.N && i >= s_lo && i <= s_hi) ? (pg[it] | (i << 16)) : -1;
     }
 #pragma unroll
     for (int it = 0; it < MAXIT; ++it)
@@ -322,8 +326,9 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
     my_slot = e.y & 0x3FFFFFFF;
     kind = (e.y >> 30) & 3;                 // bit 0: the pair's first page selected, bit 1: second
   }
-  const uint32_t m0 = (uint32_t)__ballot(kind & 1) & 0xFFu;
-  const uint32_t m1 = (uint32_t)__ballot(kind & 2) & 0xFFu;
+  const uint32_t own = ((2u << s_hi) - (1u << s_lo)) & 0xFFu;    // this wave's slots
+  const uint32_t m0 = (uint32_t)__ballot(kind & 1) & own;
+  const uint32_t m1 = (uint32_t)__ballot(kind & 2) & own;
   if (m0) list[n_u++] = (uint32_t)pa | (m0 << 16);
   if (m1) list[n_u++] = (uint32_t)pb | (m1 << 16);
   wave_sync();
