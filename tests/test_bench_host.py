@@ -37,3 +37,31 @@ def test_pair_entries_adjacent_and_table():
     pairs = np.full((1, 6, 2), -1, np.int32)
     pairs[0, :3] = [[0, 2], [1, 3], [4, 5]]
     assert bench.pair_entries(sel, pairs, 6) == 2.5
+
+
+def test_tile_units_by_hand_and_brute_force():
+    # one head, a group of 4 queries at G = 16: 64 rows in two 32-row tiles of 2 slots each
+    sel = np.array([[[0, 1], [1, 2], [3, 3], [4, -1]]], dtype=np.int32)
+    ids = np.array([[0, 1, 2, 3]], dtype=np.int32)
+    # tile 0: queries 0, 1 -> {0, 1, 2}; tile 1: queries 2, 3 -> {3, 4}; the group union has 5
+    assert bench.tile_units(sel, ids, 4, 16, N=8) == 5
+    assert bench.tile_units(sel, ids, 4, 8, N=8) == 5         # one tile: the group union
+    assert bench.union_stats(sel, ids, 4, N=8).sum() == 5
+    assert bench.tile_units(np.array([[[0, 1], [0, 1], [0, 1], [0, 1]]], np.int32), ids, 4, 16, 8) == 4
+    # random cases against a set-based count
+    rng = np.random.default_rng(3)
+    H, T, S, N = 2, 64, 5, 40
+    sel = rng.integers(-1, N, size=(H, T, S)).astype(np.int32)
+    ids = np.stack([rng.permutation(T) for _ in range(H)]).astype(np.int32)
+    for g, G in [(8, 4), (8, 8), (16, 4), (5, 8), (3, 32), (7, 8)]:
+        want = 0
+        for h in range(H):
+            for k0 in range(0, T, g):
+                mem = ids[h, k0:k0 + g]
+                for rt in range((g * G + 31) // 32):
+                    pages = set()
+                    for s in range(len(mem)):
+                        if (32 * rt) // G <= s <= (32 * rt + 31) // G:
+                            pages |= {int(u) for u in sel[h, mem[s]] if 0 <= u < N}
+                    want += len(pages)
+        assert bench.tile_units(sel, ids, g, G, N) == want, (g, G)
