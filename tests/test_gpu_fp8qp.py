@@ -135,24 +135,25 @@ def test_edge_cases_in_selection():
     assert np.all(o[100, 0:4] == 0) and np.all(o[7, 4:8] == 0)
 
 
-def test_large_sampled():
-    # the benchmark's 64K workload in the benchmark's launch (search with its group order, the
-    # re-tiling, the variant in that order): every 32nd window of every head, the first and last
-    # two windows and 48 random queries per head
+@pytest.mark.parametrize("name,every", [("prefill_64k", 32), ("prefill_64k_70b", 64)])
+def test_large_sampled(name, every):
+    # the 64K workloads in the benchmark's launch (search with its group order, the re-tiling,
+    # the variant in that order; at 70B-like two row tiles per group): every 32nd (64th) window
+    # of every head, the first and last two windows and 48 random queries per head
     pw = _pw()
-    wl = synth.WORKLOADS["prefill_64k"]
-    inp = host_inputs("prefill_64k")
-    pairs = window_sample_pairs(wl, every=32, n_random=48)
-    log(f"[case] fp8qp prefill_64k: {len(pairs)} sampled rows")
+    wl = synth.WORKLOADS[name]
+    inp = host_inputs(name)
+    pairs = window_sample_pairs(wl, every=every, n_random=48)
+    log(f"[case] fp8qp {name}: {len(pairs)} sampled rows")
     shp = pw.shape(*wl.shape_tuple())
     dev = pw.to_device(inp)
     ids, order = pw.pw_group_ordered(shp, dev["sel_pages"], wl.W, wl.g)
     O, _, _ = _run(inp, wl.g, ids, order=order, dev=dev)
     got = gpu_rows(O, pairs, wl.G)
-    assert_close_lowp(got, model_rows(inp, pairs), "prefill_64k")
+    assert_close_lowp(got, model_rows(inp, pairs), name)
     few = sample_pairs(wl, n_windows=1, n_random=32)
     e = errors(gpu_rows(O, few, wl.G), oracle_rows(inp, few))
-    log(f"[accuracy] fp8qp vs exact attention, prefill_64k: max {e['max']:.3e} "
+    log(f"[accuracy] fp8qp vs exact attention, {name}: max {e['max']:.3e} "
         f"mean {e['mean']:.3e} rel_rms {e['rel_rms']:.3e}")
 
 
