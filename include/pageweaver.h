@@ -64,6 +64,10 @@
  *             Scales must be positive and finite.
  *   O         bf16  [T][H_q][D]      output, one writer per row.
  *
+ * Alignment (else PW_ERR_DIMS): Q, K_fp8, V_fp8 and O 16 bytes (their rows
+ * move 16 bytes at a time); sel_pages 16 bytes when S is a multiple of 4,
+ * else 4; page pairs 8; every other int32 / fp32 array 4.
+ *
  * e4m3fn is the OCP 8-bit E4M3 format with a NaN and no infinities (max 448).
  */
 #ifndef PAGEWEAVER_H

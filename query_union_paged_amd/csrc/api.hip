@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <initializer_list>
+
 #include "pw_internal.h"
 
 namespace {
@@ -54,6 +56,22 @@ pw_status check_attention_support(const pw_shape* s, int g) {
   return PW_OK;
 }
 
+// The kernels move whole vectors: rows of Q, K, V and O 16 bytes at a time, selection rows 16
+// bytes at a time when S is a multiple of 4, page pairs as 8-byte pairs, and the other int32 /
+// fp32 arrays element by element.  NULL entries are checked elsewhere.
+struct Aligned {
+  const char* name;
+  const void* p;
+  unsigned bytes;
+};
+pw_status check_aligned(std::initializer_list<Aligned> xs) {
+  for (const Aligned& x : xs)
+    if (x.p != nullptr && ((uintptr_t)x.p & (x.bytes - 1)) != 0)
+      return fail(PW_ERR_DIMS, "%s must be %u-byte aligned", x.name, x.bytes);
+  return PW_OK;
+}
+unsigned sel_align(const pw_shape* s) { return s->S % 4 == 0 ? 16u : 4u; }
+
 // The re-tiled K/V copy of pw_tile_kv: size, alignment, and the 2 GiB reach of
 // the 32-bit offsets its readers form.
 pw_status check_tiled_workspace(const pw_shape* s, const void* ws, size_t ws_bytes) {
@@ -101,7 +119,7 @@ static pw_status check_group_args(const pw_shape* shape, const int32_t* sel_page
                 "W = %d is not a multiple of g = %d (attention groups would straddle windows)", W, g);
   if (shape->N_pages > 1024)
     return fail(PW_ERR_UNSUPPORTED, "N_pages = %d exceeds 1024 for the search", shape->N_pages);
-  return PW_OK;
+  return check_aligned({{"sel_pages", sel_pages, sel_align(shape)}, {"query_ids", query_ids, 4}});
 }
 
 pw_status pw_group(const pw_shape* shape, const int32_t* sel_pages, int32_t W, int32_t g,
@@ -148,6 +166,8 @@ pw_status pw_check_ids(const pw_shape* shape, const int32_t* query_ids, int32_t*
   pw_status st = check_shape(shape);
   if (st != PW_OK) return st;
   if (!query_ids || !bad_counts) return fail(PW_ERR_NULL, "query_ids and bad_counts are required");
+  st = check_aligned({{"query_ids", query_ids, 4}, {"bad_counts", bad_counts, 4}});
+  if (st != PW_OK) return st;
   const size_t need = pw::check_ids_workspace(*shape);
   if (!ws) return fail(PW_ERR_NULL, "workspace of %zu bytes required", need);
   if (ws_bytes < need) return fail(PW_ERR_WORKSPACE, "workspace %zu < %zu bytes", ws_bytes, need);
@@ -170,6 +190,10 @@ static pw_status union_attention_range(const pw_shape* shape, const uint16_t* Q,
   if (st != PW_OK) return st;
   if (!Q || !K_fp8 || !V_fp8 || !scales || !sel_pages || !query_ids || !O)
     return fail(PW_ERR_NULL, "Q, K_fp8, V_fp8, scales, sel_pages, query_ids and O are required");
+  st = check_aligned({{"Q", Q, 16}, {"K_fp8", K_fp8, 16}, {"V_fp8", V_fp8, 16}, {"scales", scales, 4},
+                      {"sel_pages", sel_pages, sel_align(shape)}, {"query_ids", query_ids, 4},
+                      {"O", O, 16}});
+  if (st != PW_OK) return st;
   st = check_attention_support(shape, g);
   if (st != PW_OK) return st;
   if (h_begin < 0 || h_count < 1 || h_begin + h_count > shape->H_kv)
@@ -211,6 +235,10 @@ pw_status pw_union_attention_noalloc(const pw_shape* shape, const uint16_t* Q,
   if (st != PW_OK) return st;
   if (!Q || !K_fp8 || !V_fp8 || !scales || !sel_pages || !query_ids || !O)
     return fail(PW_ERR_NULL, "Q, K_fp8, V_fp8, scales, sel_pages, query_ids and O are required");
+  st = check_aligned({{"Q", Q, 16}, {"K_fp8", K_fp8, 16}, {"V_fp8", V_fp8, 16}, {"scales", scales, 4},
+                      {"sel_pages", sel_pages, sel_align(shape)}, {"query_ids", query_ids, 4},
+                      {"O", O, 16}});
+  if (st != PW_OK) return st;
   st = check_attention_support(shape, g);
   if (st != PW_OK) return st;
   const size_t need = pw::tiled_kv_bytes(*shape);
@@ -235,6 +263,8 @@ pw_status pw_tile_kv(const pw_shape* shape, const uint8_t* K_fp8, const uint8_t*
   pw_status st = check_shape(shape);
   if (st != PW_OK) return st;
   if (!K_fp8 || !V_fp8 || !scales) return fail(PW_ERR_NULL, "K_fp8, V_fp8 and scales are required");
+  st = check_aligned({{"K_fp8", K_fp8, 16}, {"V_fp8", V_fp8, 16}, {"scales", scales, 4}});
+  if (st != PW_OK) return st;
   st = check_attention_support(shape, 1);
   if (st != PW_OK) return st;
   st = check_tiled_workspace(shape, ws, ws_bytes);
@@ -253,6 +283,9 @@ static pw_status tiled_attention(const pw_shape* shape, const uint16_t* Q,
   if (st != PW_OK) return st;
   if (!Q || !sel_pages || !query_ids || !O)
     return fail(PW_ERR_NULL, "Q, sel_pages, query_ids and O are required");
+  st = check_aligned({{"Q", Q, 16}, {"sel_pages", sel_pages, sel_align(shape)},
+                      {"query_ids", query_ids, 4}, {"group_order", group_order, 4}, {"O", O, 16}});
+  if (st != PW_OK) return st;
   st = check_attention_support(shape, g);
   if (st != PW_OK) return st;
   st = check_tiled_workspace(shape, ws, ws_bytes);
@@ -299,6 +332,9 @@ pw_status pw_dense_union_ref(const pw_shape* shape, const uint16_t* Q, const uin
   if (st != PW_OK) return st;
   if (!Q || !K_fp8 || !V_fp8 || !scales || !sel_pages || !O)
     return fail(PW_ERR_NULL, "Q, K_fp8, V_fp8, scales, sel_pages and O are required");
+  st = check_aligned({{"Q", Q, 16}, {"K_fp8", K_fp8, 16}, {"V_fp8", V_fp8, 16}, {"scales", scales, 4},
+                      {"sel_pages", sel_pages, sel_align(shape)}, {"O", O, 16}});
+  if (st != PW_OK) return st;
   st = check_attention_support(shape, 1);
   if (st != PW_OK) return st;
   if (shape->H_q / shape->H_kv > 8)
@@ -325,6 +361,9 @@ pw_status pw_dense_union_paired(const pw_shape* shape, const uint16_t* Q, const 
   if (st != PW_OK) return st;
   if (!Q || !K_fp8 || !V_fp8 || !scales || !sel_pages || !pairs || !O)
     return fail(PW_ERR_NULL, "Q, K_fp8, V_fp8, scales, sel_pages, pairs and O are required");
+  st = check_aligned({{"Q", Q, 16}, {"K_fp8", K_fp8, 16}, {"V_fp8", V_fp8, 16}, {"scales", scales, 4},
+                      {"sel_pages", sel_pages, sel_align(shape)}, {"pairs", pairs, 8}, {"O", O, 16}});
+  if (st != PW_OK) return st;
   st = check_attention_support(shape, 1);
   if (st != PW_OK) return st;
   if (shape->H_q / shape->H_kv > 8)
@@ -353,6 +392,8 @@ pw_status pw_page_pairs(const pw_shape* shape, const int32_t* sel_pages, int32_t
   pw_status st = check_shape(shape);
   if (st != PW_OK) return st;
   if (!sel_pages || !pairs) return fail(PW_ERR_NULL, "sel_pages and pairs are required");
+  st = check_aligned({{"sel_pages", sel_pages, sel_align(shape)}, {"pairs", pairs, 8}});
+  if (st != PW_OK) return st;
   if (shape->N_pages > 2048)
     return fail(PW_ERR_UNSUPPORTED, "N_pages = %d exceeds 2048 for the pairing", shape->N_pages);
   if (shape->T >= (1 << 19))
@@ -379,6 +420,9 @@ pw_status pw_select(const pw_shape* shape, const uint16_t* Q, const uint8_t* K_f
   if (st != PW_OK) return st;
   if (!Q || !K_fp8 || !scales || !sel_pages)
     return fail(PW_ERR_NULL, "Q, K_fp8, scales and sel_pages are required");
+  st = check_aligned({{"Q", Q, 16}, {"K_fp8", K_fp8, 16}, {"scales", scales, 4},
+                      {"sel_pages", sel_pages, sel_align(shape)}});
+  if (st != PW_OK) return st;
   if (shape->D != 64 && shape->D != 128)
     return fail(PW_ERR_UNSUPPORTED, "D = %d not in {64, 128}", shape->D);
   if (shape->P != 16 && shape->P != 32 && shape->P != 64)

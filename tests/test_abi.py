@@ -222,3 +222,34 @@ def test_binding_refuses_host_tensors():
     shp = _shape()
     with pytest.raises(TypeError):
         pw.pw_group(shp, torch.zeros((1, 1024, 8), dtype=torch.int32), 32, 8)
+
+
+def test_alignment_validation():
+    # misaligned pointers are refused before any HIP call, naming the argument
+    odd16, odd4 = ctypes.c_void_p(0x1008), ctypes.c_void_p(0x1002)
+    shp = _shape()                                      # S = 8: selection rows read 16 B at a time
+    for i, name in [(0, b"Q"), (1, b"K_fp8"), (2, b"V_fp8"), (6, b"O")]:
+        ptrs = [FAKE] * 7
+        ptrs[i] = odd16
+        assert _attn(shp, ptrs=ptrs) == pw.PW_ERR_DIMS
+        assert name in pw._lib.pw_last_error()
+    for i, name in [(3, b"scales"), (5, b"query_ids")]:
+        ptrs = [FAKE] * 7
+        ptrs[i] = odd4
+        assert _attn(shp, ptrs=ptrs) == pw.PW_ERR_DIMS
+        assert name in pw._lib.pw_last_error()
+    ptrs = [FAKE] * 7
+    ptrs[4] = odd16
+    assert _attn(shp, ptrs=ptrs) == pw.PW_ERR_DIMS          # sel_pages, S a multiple of 4
+    assert _group(shp, sel=odd16) == pw.PW_ERR_DIMS
+    # S = 6: 4-byte alignment suffices (pw_group_ordered then stops at the missing group_order)
+    assert pw._lib.pw_group_ordered(ctypes.byref(_shape(S=6)), odd16, 32, 8, FAKE, None, FAKE,
+                                    1 << 20, None) == pw.PW_ERR_NULL
+    assert _group(_shape(S=6), sel=odd4) == pw.PW_ERR_DIMS
+    assert _group(shp, ids=odd4) == pw.PW_ERR_DIMS
+    assert pw._lib.pw_tile_kv(ctypes.byref(shp), FAKE, odd16, FAKE, FAKE, 1 << 30, None) == pw.PW_ERR_DIMS
+    assert pw._lib.pw_union_attention_tiled_fp8qp(ctypes.byref(shp), FAKE, FAKE, FAKE, odd4, 8,
+                                                  FAKE, FAKE, 1 << 30, None) == pw.PW_ERR_DIMS
+    assert b"group_order" in pw._lib.pw_last_error()
+    assert pw._lib.pw_page_pairs(ctypes.byref(shp), FAKE, odd4, FAKE, 1 << 30, None) == pw.PW_ERR_DIMS
+    assert b"pairs" in pw._lib.pw_last_error()
