@@ -253,3 +253,36 @@ def test_alignment_validation():
     assert b"group_order" in pw._lib.pw_last_error()
     assert pw._lib.pw_page_pairs(ctypes.byref(shp), FAKE, odd4, FAKE, 1 << 30, None) == pw.PW_ERR_DIMS
     assert b"pairs" in pw._lib.pw_last_error()
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    # the boundary needs nothing but C: the header compiles as C99 and as C++, and a C program
+    # links the library and gets statuses back (validation only; no HIP call is made)
+    import os
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    inc = os.path.join(root, "include")
+    src = tmp_path / "use.c"
+    src.write_text(
+        '#include <stdio.h>\n#include "pageweaver.h"\n'
+        "int main(void) {\n"
+        "  pw_shape s = {1024, 4, 1, 64, 16, 64, 8};\n"
+        "  int32_t ids[1];\n"
+        "  if (pw_abi_version() != PW_ABI_VERSION) return 1;\n"
+        "  if (pw_group(NULL, NULL, 32, 8, ids, NULL, 0, NULL) != PW_ERR_NULL) return 2;\n"
+        "  if (pw_group(&s, NULL, 32, 8, ids, NULL, 0, NULL) != PW_ERR_NULL) return 3;\n"
+        "  if (pw_union_attention_workspace_bytes(&s, 8) == 0) return 4;\n"
+        '  printf("%s\\n", pw_status_string(PW_ERR_DIMS));\n'
+        "  return 0;\n}\n")
+    for cmd in (["gcc", "-std=c99", "-Wall", "-Wextra", "-Werror", "-fsyntax-only", "-x", "c",
+                 "-I", inc, os.path.join(inc, "pageweaver.h")],
+                ["g++", "-std=c++17", "-Wall", "-Werror", "-fsyntax-only", "-x", "c++",
+                 "-I", inc, os.path.join(inc, "pageweaver.h")]):
+        subprocess.run(cmd, check=True, capture_output=True, text=True)
+    exe = tmp_path / "use"
+    libdir = os.path.dirname(pw.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", inc, str(src), "-o", str(exe),
+                    "-L", libdir, "-l:" + os.path.basename(pw.LIB_PATH),
+                    "-Wl,-rpath," + libdir], check=True, capture_output=True, text=True)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stderr)
+    assert r.stdout.strip() == "invalid dimensions"
