@@ -92,11 +92,25 @@ __device__ __forceinline__ void window_body(const int32_t* __restrict__ wbase, i
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
+          // the four entries belong to one row (S is a multiple of 4) and selection rows are
+          // usually sorted: entries that fall into the same bitset word share one LDS atomic
           const int r = ((i0 + 64 * j + lane) << 2) / S;
-          put(r, v[j].x);
-          put(r, v[j].y);
-          put(r, v[j].z);
-          put(r, v[j].w);
+          const int e4[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+          int wcur = -1;
+          uint32_t bits = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int u = e4[q];
+            const int k = (u >= 0 && u < N) ? (rank != nullptr ? (int)rank[u] : u) : -1;
+            const int wq = k >= 0 ? (k >> 5) : -1;
+            if (wq != wcur) {
+              if (bits) atomicOr(&stage[r * kStride + wcur], bits);
+              wcur = wq;
+              bits = 0;
+            }
+            if (k >= 0) bits |= 1u << (k & 31);
+          }
+          if (bits) atomicOr(&stage[r * kStride + wcur], bits);
         }
       }
     } else {
@@ -274,10 +288,22 @@ __global__ __launch_bounds__(64 * NWV) void group_kernel(const int32_t* __restri
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
+        // one LDS atomic per run of entries in the same word of the page set
         const int e[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+        int wcur = -1;
+        uint32_t bits = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          if (e[k] >= 0 && e[k] < N) atomicOr(&apg[e[k] >> 5], 1u << (e[k] & 31));
+        for (int k = 0; k < 4; ++k) {
+          const bool ok = e[k] >= 0 && e[k] < N;
+          const int wq = ok ? (e[k] >> 5) : -1;
+          if (wq != wcur) {
+            if (bits) atomicOr(&apg[wcur], bits);
+            wcur = wq;
+            bits = 0;
+          }
+          if (ok) bits |= 1u << (e[k] & 31);
+        }
+        if (bits) atomicOr(&apg[wcur], bits);
       }
     }
   } else {
