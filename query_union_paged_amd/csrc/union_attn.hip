@@ -252,18 +252,50 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   int pg[MAXIT];
   {
     const int n_ent = gm * p.S;
+    if ((p.S & 3) == 0) {
+      // lane l takes slots 4 (l + 64 j) .. + 3, four consecutive slots of one member (one
+      // 16-byte load); selection rows are usually sorted, so entries in the same bitset word
+      // share one LDS atomic
 #pragma unroll
-    for (int it = 0; it < MAXIT; ++it) {
-      const int e = lane + 64 * it;
-      const int i = e / p.S;
-      const int t = __shfl(my_t, i & 63);
-      pg[it] = -1;
-      if (e < n_ent && t >= 0) pg[it] = p.sel[((size_t)h * p.T + t) * p.S + (e - i * p.S)];
-      pg[it] = (pg[it] >= 0 && pg[it] < p.N && i >= s_lo && i <= s_hi) ? (pg[it] | (i << 16)) : -1;
+      for (int j = 0; j < MAXIT / 4; ++j) {
+        const int e0 = 4 * (lane + 64 * j);
+        const int i = e0 / p.S;
+        const int t = __shfl(my_t, i & 63);
+        int4 v = make_int4(-1, -1, -1, -1);
+        if (e0 < n_ent && t >= 0)
+          v = *reinterpret_cast<const int4*>(p.sel + ((size_t)h * p.T + t) * p.S + (e0 - i * p.S));
+        const int e4[4] = {v.x, v.y, v.z, v.w};
+        int wcur = -1;
+        uint32_t word_bits = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int u = e4[q];
+          const bool ok = u >= 0 && u < p.N && i >= s_lo && i <= s_hi;
+          pg[4 * j + q] = ok ? (u | (i << 16)) : -1;
+          const int wq = ok ? (u >> 5) : -1;
+          if (wq != wcur) {
+            if (word_bits) atomicOr(&bits[wcur], word_bits);
+            wcur = wq;
+            word_bits = 0;
+          }
+          if (ok) word_bits |= 1u << (u & 31);
+        }
+        if (word_bits) atomicOr(&bits[wcur], word_bits);
+      }
+    } else {
+#pragma unroll
+      for (int it = 0; it < MAXIT; ++it) {
+        const int e = lane + 64 * it;
+        const int i = e / p.S;
+        const int t = __shfl(my_t, i & 63);
+        pg[it] = -1;
+        if (e < n_ent && t >= 0) pg[it] = p.sel[((size_t)h * p.T + t) * p.S + (e - i * p.S)];
+        pg[it] = (pg[it] >= 0 && pg[it] < p.N && i >= s_lo && i <= s_hi) ? (pg[it] | (i << 16)) : -1;
+      }
+#pragma unroll
+      for (int it = 0; it < MAXIT; ++it)
+        if (pg[it] >= 0) atomicOr(&bits[(pg[it] & 0xFFFF) >> 5], 1u << (pg[it] & 31));
     }
-#pragma unroll
-    for (int it = 0; it < MAXIT; ++it)
-      if (pg[it] >= 0) atomicOr(&bits[(pg[it] & 0xFFFF) >> 5], 1u << (pg[it] & 31));
   }
   wave_sync();
   for (int c0 = 0; c0 < nw; c0 += 64) {
