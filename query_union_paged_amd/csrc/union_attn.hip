@@ -393,9 +393,6 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   uint4 kbuf[2][KCH], vbuf[DT][2];
   f32x16 sacc[2];
   float4 pfr = make_float4(0.f, 0.f, 0.f, 0.f);
-  auto page_of = [&](int i) {       // wave-uniform
-    return __builtin_amdgcn_readfirstlane((int)(list[min(i, n_u - 1)] & 0xFFFF));
-  };
   const int block_bytes = 64 * D;
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)p.Kt, (short)0, 0x7FFFFFFF, 0x00020000);
@@ -429,8 +426,14 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   // and vector work.  (Software-pipelined schedules that keep the next page's
   // scores in flight during the softmax need more than the 256 registers a
   // wave has at this occupancy; they spilled and ran slower.)
+  // The list entry of the next page (page in the low half, member mask in the
+  // high half) is read once, one page ahead, and carried into the next step:
+  // one LDS read per page, and none after the page factors' scalar load, whose
+  // wait therefore falls a whole page later.
+  uint32_t ent_nx = 0;
   if (n_u > 0) {
-    const int u0 = page_of(0);
+    ent_nx = (uint32_t)__builtin_amdgcn_readfirstlane((int)list[0]);
+    const int u0 = (int)(ent_nx & 0xFFFF);
     load_k(kbuf, u0);
     load_v(vbuf, u0);
     pfr = pfac[(size_t)u0 * p.Hkv];
@@ -439,9 +442,10 @@ __global__ __launch_bounds__(64 * PW_UA_WG_WAVES, 2) void union_attn_kernel(UAPa
   i32x8 pF;
   int vsb = 127;
   for (int up = 0; up < n_u; ++up) {
-    const uint32_t ent = __builtin_amdgcn_readfirstlane(list[up]);
+    const uint32_t ent = ent_nx;
     const float4 pf_c = pfr;
-    const int u1 = page_of(up + 1);
+    ent_nx = (uint32_t)__builtin_amdgcn_readfirstlane((int)list[min(up + 1, n_u - 1)]);
+    const int u1 = (int)(ent_nx & 0xFFFF);
     qk_page<D, MODE == kFp8Mode ? 1 : 2>(kbuf, qr, sacc);
     load_k(kbuf, u1);                     // K registers are free once the MFMAs have read them
     pfr = pfac[(size_t)u1 * p.Hkv];
