@@ -135,6 +135,18 @@ def test_edge_cases_in_selection():
     assert np.all(o[100, 0:4] == 0) and np.all(o[7, 4:8] == 0)
 
 
+def test_edge_cases_in_selection_four_slot_loads():
+    # S % 4 == 0 (the union build's 16-byte loads of four slots), two bitset words
+    from tests.test_gpu_union_attn import four_slot_edge_selection
+    log("[case] fp8qp selection edge cases, S = 8, N = 64")
+    inp = four_slot_edge_selection(83)
+    O, _, _ = _run(inp, 8, W=64)
+    pairs = [(h, t) for h in range(2) for t in range(1024)]
+    assert_close_lowp(gpu_rows(O, pairs, 4), model_rows(inp, pairs), "edge cases, S = 8")
+    o = O.float().cpu().numpy()
+    assert np.all(o[100, 0:4] == 0) and np.all(o[7, 4:8] == 0)
+
+
 @pytest.mark.parametrize("name,every", [("prefill_64k", 32), ("prefill_64k_70b", 64)])
 def test_large_sampled(name, every):
     # the 64K workloads in the benchmark's launch (search with its group order, the re-tiling,

@@ -118,6 +118,35 @@ def test_edge_cases_in_selection():
     assert np.all(o[100, 0:4] == 0) and np.all(o[7, 4:8] == 0)
 
 
+def four_slot_edge_selection(seed):
+    """T = 1024, P = 16 (N = 64 pages: two bitset words), S = 8 (each member row is two 16-byte
+    loads of four slots): invalid slots between valid ones, repeats, out-of-range and future
+    pages, unsorted rows alternating between the two words, a row of one page."""
+    T, P, S = 1024, 16, 8
+    inp = tiny_problem(T=T, Hq=8, Hkv=2, D=128, P=P, S=S, seed=seed)
+    sel = inp["sel_pages"].copy()
+    sel[0, 100] = -1                                    # empty support -> O = 0
+    sel[1, 7] = [40, 63, -1, 99, -7, 33, 64, 2]         # only future / out-of-range pages -> O = 0
+    sel[0, 300] = [18, 18, 0, 0, 37, -1, 5, 5]          # repeats around an invalid slot
+    sel[1, 511] = [33, 2, 40, 1, 63, 32, 0, 31]         # unsorted, alternating words
+    sel[0, 900] = [49, 50, -1, 51, 49, 99, 52, 50]      # a same-word run cut by invalid slots
+    sel[1, 1000] = 56                                   # one page in every slot
+    sel[0, 40:48] = sel[0, 40:48][:, ::-1]              # descending rows
+    return dict(inp, sel_pages=sel)
+
+
+def test_edge_cases_in_selection_four_slot_loads():
+    # S % 4 == 0: the union build reads four slots of a member with one 16-byte load and ORs
+    # the entries of one bitset word with one LDS atomic
+    log("[case] union selection edge cases, S = 8, N = 64")
+    inp = four_slot_edge_selection(81)
+    O, _ = _run(inp, 8, "regroup", 64)
+    pairs = _all_pairs(2, 1024)
+    assert_close(gpu_rows(O, pairs, 4), oracle_rows(inp, pairs), "edge cases, S = 8")
+    o = O.float().cpu().numpy()
+    assert np.all(o[100, 0:4] == 0) and np.all(o[7, 4:8] == 0)
+
+
 @pytest.mark.parametrize("name,arms", [("prefill_32k", ["regroup", "identity"]),
                                        ("prefill_64k", ["regroup", "identity", "g1"]),
                                        ("prefill_64k_70b", ["regroup", "identity"])])
