@@ -141,9 +141,12 @@ def recorded_traffic(workload: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("kernel_sha256_16") != kernel_hash() or rec.get("workload") != workload:
+    if rec.get("kernel_sha256_16") != kernel_hash():
         return None
-    return rec.get("dram_bytes_per_launch")
+    per = rec.get("workloads", {}).get(workload)
+    if per is not None:
+        return per.get("dram_bytes_per_launch")
+    return rec.get("dram_bytes_per_launch") if rec.get("workload") == workload else None
 
 
 def cpu_baseline(inp, wl, seconds: float):

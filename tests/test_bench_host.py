@@ -65,3 +65,33 @@ def test_tile_units_by_hand_and_brute_force():
                             pages |= {int(u) for u in sel[h, mem[s]] if 0 <= u < N}
                     want += len(pages)
         assert bench.tile_units(sel, ids, g, G, N) == want, (g, G)
+
+
+def test_recorded_traffic_per_workload_and_stale_hash(tmp_path, monkeypatch):
+    # DRAM bytes come from the stored counter record only while its kernel hash matches the
+    # current sources, and per workload; an unknown workload or a stale hash gives None
+    import json
+    rec = {"kernel_sha256_16": bench.kernel_hash(), "workload": "prefill_64k",
+           "dram_bytes_per_launch": 5.0,
+           "workloads": {"prefill_8k": {"dram_bytes_per_launch": 1.0},
+                         "prefill_64k": {"dram_bytes_per_launch": 2.0}}}
+    (tmp_path / "profiles").mkdir()
+    f = tmp_path / "profiles" / "union_attn_counters.json"
+    f.write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "kernel_hash", lambda: rec["kernel_sha256_16"])
+    assert bench.recorded_traffic("prefill_8k") == 1.0
+    assert bench.recorded_traffic("prefill_64k") == 2.0
+    assert bench.recorded_traffic("prefill_32k") is None
+    monkeypatch.setattr(bench, "kernel_hash", lambda: "0" * 16)
+    assert bench.recorded_traffic("prefill_8k") is None
+
+
+def test_stored_counters_match_the_current_kernel():
+    # the committed counter record was taken on the current attention sources and build flags
+    import json
+    rec = json.load(open(os.path.join(ROOT, "profiles", "union_attn_counters.json")))
+    assert rec["kernel_sha256_16"] == bench.kernel_hash()
+    for wl in ("prefill_8k", "prefill_32k", "prefill_64k", "prefill_64k_70b"):
+        per = rec["workloads"][wl]
+        assert per["dram_bytes_per_launch"] >= per["compulsory_bytes"] > 0
